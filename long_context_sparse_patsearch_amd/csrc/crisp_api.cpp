@@ -1,0 +1,218 @@
+// C-ABI entry points of libcrisp: argument validation (host only, before any
+// HIP call), workspace carving and launch sequencing on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/crisp.h"
+#include "crisp_internal.h"
+
+using crisp::Dims;
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+constexpr int kBlock = 128;
+constexpr int kMinN = 3 * kBlock;
+constexpr int kMaxN = 1 << 20;
+
+int make_dims(const crisp_shape* s, Dims* dm) {
+  if (!s) return CRISP_ERR_NULL;
+  if (s->batch < 0 || s->h_q < 1 || s->h_kv < 1 || s->h_q % s->h_kv) return CRISP_ERR_SHAPE;
+  if (s->d != 64 && s->d != 128) return CRISP_ERR_SHAPE;
+  if (s->n % kBlock || s->n < kMinN || s->n > kMaxN) return CRISP_ERR_SHAPE;
+  const int64_t bh = (int64_t)s->batch * s->h_q;
+  const int64_t nb = s->n / kBlock;
+  // grid limits: batch*h_q is a grid dimension; one workgroup of up to 256 threads per CSR row
+  if (bh > 65535 || bh * nb > (1LL << 24) - 1) return CRISP_ERR_SHAPE;
+  dm->batch = s->batch;
+  dm->n = s->n;
+  dm->h_q = s->h_q;
+  dm->h_kv = s->h_kv;
+  dm->d = s->d;
+  dm->nb = (int)nb;
+  dm->group = s->h_q / s->h_kv;
+  dm->bh = bh;
+  dm->rows = bh * nb;
+  dm->tri = nb * (nb + 1) / 2;
+  return CRISP_OK;
+}
+
+int check_cfg(const crisp_cfg* c) {
+  if (!c) return CRISP_ERR_NULL;
+  if (c->block != kBlock || c->last_q != kBlock || c->w_sink != kBlock || c->w_local != kBlock)
+    return CRISP_ERR_UNSUPPORTED;
+  if (c->k_min_tokens < 0 || c->k_min_tokens % kBlock) return CRISP_ERR_PARAM;
+  if (!std::isfinite(c->tau)) return CRISP_ERR_PARAM;
+  if (!std::isfinite(c->alpha) || !(c->alpha >= 0.f)) return CRISP_ERR_PARAM;
+  if (!(c->gamma > 0.f && c->gamma <= 1.f)) return CRISP_ERR_PARAM;
+  return CRISP_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct RouteWs {
+  float* part;
+  float* stats;
+  float* lu;
+};
+
+size_t route_ws_layout(const Dims& dm, RouteWs* w, char* base) {
+  const int nch = crisp::proxy_num_chunks(dm);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  RouteWs r{};
+  r.part = (float*)take((size_t)dm.bh * nch * kBlock * 2 * sizeof(float));
+  r.stats = (float*)take((size_t)dm.bh * kBlock * 2 * sizeof(float));
+  r.lu = (float*)take((size_t)dm.bh * dm.nb * 2 * sizeof(float));
+  if (w) *w = r;
+  return off;
+}
+
+size_t ws_bytes_for(const Dims& dm, int call) {
+  switch (call) {
+    case CRISP_CALL_ROUTE: return route_ws_layout(dm, nullptr, nullptr);
+    case CRISP_CALL_SELECT: return crisp::select_ws_layout(dm, nullptr, nullptr);
+    case CRISP_CALL_ATTN: return 0;
+    default: return (size_t)-1;
+  }
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return CRISP_OK;
+  std::snprintf(g_err, sizeof(g_err), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return CRISP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int crisp_workspace_bytes(const crisp_shape* shape, const crisp_cfg* cfg, int call, size_t* bytes) {
+  Dims dm;
+  int st = make_dims(shape, &dm);
+  if (st) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if (!bytes) return CRISP_ERR_NULL;
+  const size_t b = ws_bytes_for(dm, call);
+  if (b == (size_t)-1) return CRISP_ERR_PARAM;
+  *bytes = dm.batch ? b : 0;
+  return CRISP_OK;
+}
+
+int crisp_max_blocks(const crisp_shape* shape, int64_t* blocks) {
+  Dims dm;
+  const int st = make_dims(shape, &dm);
+  if (st) return st;
+  if (!blocks) return CRISP_ERR_NULL;
+  *blocks = dm.bh * dm.tri;
+  return CRISP_OK;
+}
+
+int crisp_route(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
+                float* c_struct, int8_t* pattern, float* p_vert, float* p_slash, void* ws, size_t ws_bytes,
+                void* stream) {
+  Dims dm;
+  int st = make_dims(shape, &dm);
+  if (st) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if (dm.batch == 0) return CRISP_OK;
+  if (!q_bf16 || !k_bf16 || !c_struct || !pattern || !p_vert || !p_slash || !ws) return CRISP_ERR_NULL;
+  if (misaligned(q_bf16) || misaligned(k_bf16) || misaligned(c_struct) || misaligned(pattern) ||
+      misaligned(p_vert) || misaligned(p_slash) || misaligned(ws))
+    return CRISP_ERR_ALIGN;
+  RouteWs w;
+  if (ws_bytes < route_ws_layout(dm, &w, static_cast<char*>(ws))) return CRISP_ERR_WORKSPACE;
+  return hip_status(crisp::launch_route(dm, cfg->tau, static_cast<const uint16_t*>(q_bf16),
+                                        static_cast<const uint16_t*>(k_bf16), c_struct, pattern, p_vert, p_slash,
+                                        w.part, w.stats, w.lu, static_cast<hipStream_t>(stream)));
+}
+
+int crisp_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
+                 const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
+                 int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws, size_t ws_bytes,
+                 void* stream) {
+  Dims dm;
+  int st = make_dims(shape, &dm);
+  if (st) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if (dm.batch == 0) return CRISP_OK;
+  if (!q_bf16 || !k_bf16 || !pattern || !p_vert || !p_slash || !row_ptr || !col_idx || !ws) return CRISP_ERR_NULL;
+  if (misaligned(q_bf16) || misaligned(k_bf16) || misaligned(pattern) || misaligned(p_vert) ||
+      misaligned(p_slash) || misaligned(row_ptr) || misaligned(col_idx) || misaligned(ws) ||
+      (sel_mask && misaligned(sel_mask)))
+    return CRISP_ERR_ALIGN;
+  crisp::SelectWs w;
+  if (ws_bytes < crisp::select_ws_layout(dm, &w, static_cast<char*>(ws))) return CRISP_ERR_WORKSPACE;
+  if (col_capacity < dm.bh * dm.tri) return CRISP_ERR_CAPACITY;
+  return hip_status(crisp::launch_select(dm, cfg->alpha, cfg->gamma, cfg->k_min_tokens / kBlock,
+                                         static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(k_bf16),
+                                         pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask, w,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
+                      const void* v_bf16, const int64_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                      void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  Dims dm;
+  int st = make_dims(shape, &dm);
+  if (st) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if (out_dtype != CRISP_OUT_F32 && out_dtype != CRISP_OUT_BF16) return CRISP_ERR_PARAM;
+  if (col_capacity < 0) return CRISP_ERR_PARAM;
+  if (dm.batch == 0) return CRISP_OK;
+  if (!q_bf16 || !k_bf16 || !v_bf16 || !row_ptr || !out) return CRISP_ERR_NULL;
+  if (col_capacity > 0 && !col_idx) return CRISP_ERR_NULL;
+  if (misaligned(q_bf16) || misaligned(k_bf16) || misaligned(v_bf16) || misaligned(row_ptr) ||
+      (col_idx && misaligned(col_idx)) || misaligned(out) || (ws && misaligned(ws)))
+    return CRISP_ERR_ALIGN;
+  if (ws_bytes < ws_bytes_for(dm, CRISP_CALL_ATTN)) return CRISP_ERR_WORKSPACE;
+  (void)ws;
+  return hip_status(crisp::launch_sparse_attn(dm, static_cast<const uint16_t*>(q_bf16),
+                                              static_cast<const uint16_t*>(k_bf16),
+                                              static_cast<const uint16_t*>(v_bf16), row_ptr, col_idx, col_capacity,
+                                              out, out_dtype == CRISP_OUT_BF16, static_cast<hipStream_t>(stream)));
+}
+
+int dense_attn(const crisp_shape* shape, const void* q_bf16, const void* k_bf16, const void* v_bf16, void* out,
+               int out_dtype, void* stream) {
+  Dims dm;
+  const int st = make_dims(shape, &dm);
+  if (st) return st;
+  if (out_dtype != CRISP_OUT_F32 && out_dtype != CRISP_OUT_BF16) return CRISP_ERR_PARAM;
+  if (dm.batch == 0) return CRISP_OK;
+  if (!q_bf16 || !k_bf16 || !v_bf16 || !out) return CRISP_ERR_NULL;
+  if (misaligned(q_bf16) || misaligned(k_bf16) || misaligned(v_bf16) || misaligned(out)) return CRISP_ERR_ALIGN;
+  return hip_status(crisp::launch_dense_attn(dm, static_cast<const uint16_t*>(q_bf16),
+                                             static_cast<const uint16_t*>(k_bf16),
+                                             static_cast<const uint16_t*>(v_bf16), out,
+                                             out_dtype == CRISP_OUT_BF16, static_cast<hipStream_t>(stream)));
+}
+
+const char* crisp_status_string(int status) {
+  switch (status) {
+    case CRISP_OK: return "ok";
+    case CRISP_ERR_NULL: return "a required pointer is NULL";
+    case CRISP_ERR_SHAPE: return "shape outside the supported range";
+    case CRISP_ERR_PARAM: return "setting out of range";
+    case CRISP_ERR_UNSUPPORTED: return "setting not supported by this implementation";
+    case CRISP_ERR_WORKSPACE: return "workspace smaller than crisp_workspace_bytes";
+    case CRISP_ERR_CAPACITY: return "col_capacity below crisp_max_blocks";
+    case CRISP_ERR_HIP: return "HIP launch failed";
+    case CRISP_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+const char* crisp_last_error(void) { return g_err; }
+
+}  // extern "C"

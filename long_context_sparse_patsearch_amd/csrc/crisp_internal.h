@@ -1,0 +1,54 @@
+// Host-side launchers shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace crisp {
+
+struct Dims {
+  int batch, n, h_q, h_kv, d;
+  int nb;          // key/query blocks per sequence
+  int group;       // h_q / h_kv
+  int64_t bh;      // batch * h_q
+  int64_t rows;    // batch * h_q * nb (CSR rows)
+  int64_t tri;     // nb * (nb + 1) / 2 (causal cells per head)
+};
+
+// ---- routing (route.hip) ----
+// Split of the key range into chunks for the proxy passes.
+int proxy_chunk_tiles(const Dims& dm);
+int proxy_num_chunks(const Dims& dm);
+hipError_t launch_route(const Dims& dm, float tau, const uint16_t* q, const uint16_t* k,
+                        float* c_struct, int8_t* pattern, float* p_vert, float* p_slash,
+                        float* ws_part, float* ws_stats, float* ws_lu, hipStream_t st);
+
+// ---- selection (select.hip) ----
+struct SelectWs {
+  uint8_t* vsflags;     // [bh][2][nb]
+  float* qbar;          // [bh][nb][d]
+  float* kbar;          // [batch*h_kv][nb][d]
+  float* abar;          // [bh][tri]  scaled logits, then x = A_bar / nb
+  unsigned long long* hist_mass;  // [bh][2048]
+  uint32_t* hist_cnt;   // [bh][2048]
+  unsigned long long* pe_state;   // [bh][8]
+  int64_t* rowcnt;      // [rows]
+  int32_t* eqcnt;       // [rows]
+  int32_t* seltake;     // [rows]
+  int64_t* scan_part;   // [scan blocks + 1]
+};
+size_t select_ws_layout(const Dims& dm, SelectWs* ws, char* base);
+hipError_t launch_select(const Dims& dm, float alpha, float gamma, int kmin_blocks,
+                         const uint16_t* q, const uint16_t* k, const int8_t* pattern,
+                         const float* p_vert, const float* p_slash, int64_t* row_ptr,
+                         int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st);
+
+// ---- attention (attn.hip) ----
+hipError_t launch_sparse_attn(const Dims& dm, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const int64_t* row_ptr, const int32_t* col_idx,
+                              int64_t col_capacity, void* out, int out_bf16, hipStream_t st);
+hipError_t launch_dense_attn(const Dims& dm, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, void* out, int out_bf16, hipStream_t st);
+
+}  // namespace crisp

@@ -1,0 +1,145 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_patsearch_amd as crisp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "crisp.h")
+
+OK, NULL, SHAPE, PARAM, UNSUP, WS, CAP, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+FAKE = 0x10000          # an aligned address that is never dereferenced: validation fails first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(crisp.library_path()):
+        from long_context_sparse_patsearch_amd.build import build
+        build(verbose=False)
+    return crisp.load()
+
+
+def test_header_declares_the_method_calls():
+    names = declared_functions()
+    for f in ("crisp_route", "crisp_select", "crisp_sparse_attn", "dense_attn",
+              "crisp_workspace_bytes", "crisp_max_blocks", "crisp_status_string", "crisp_last_error"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(crisp.library_path())
+    for f in declared_functions():
+        assert hasattr(raw, f), f"{f} declared in crisp.h but not exported"
+
+
+def shape(batch=1, n=4096, h_q=2, h_kv=2, d=64):
+    return crisp.Shape(batch, n, h_q, h_kv, d)
+
+
+@pytest.mark.parametrize("sh,status", [
+    (shape(), OK),
+    (shape(n=4096 + 64), SHAPE), (shape(n=256), SHAPE), (shape(n=0), SHAPE), (shape(n=1 << 21), SHAPE),
+    (shape(d=96), SHAPE), (shape(h_q=3, h_kv=2), SHAPE), (shape(h_kv=0), SHAPE), (shape(batch=-1), SHAPE),
+    (shape(batch=0), OK), (shape(n=384), OK), (shape(n=1 << 20, h_q=8, h_kv=1, d=128), OK),
+])
+def test_shape_validation(lib, sh, status):
+    n = ctypes.c_size_t(7)
+    assert lib.crisp_workspace_bytes(ctypes.byref(sh), ctypes.byref(crisp.config()), 0, ctypes.byref(n)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), OK), (dict(block=64), UNSUP), (dict(k_min_tokens=100), PARAM), (dict(k_min_tokens=-128), PARAM),
+    (dict(gamma=0.0), PARAM), (dict(gamma=1.5), PARAM), (dict(gamma=1.0), OK), (dict(alpha=-0.1), PARAM),
+    (dict(alpha=0.0), OK), (dict(tau=float("nan")), PARAM), (dict(alpha=float("inf")), PARAM),
+])
+def test_cfg_validation(lib, kw, status):
+    cfg = crisp.config(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.crisp_workspace_bytes(ctypes.byref(shape()), ctypes.byref(cfg), 1, ctypes.byref(n)) == status
+
+
+def test_workspace_and_capacity_queries(lib):
+    sh = shape(batch=2, n=4096, h_q=4, h_kv=2, d=128)
+    cfg = crisp.config()
+    sizes = [crisp.workspace_bytes(sh, cfg, c) for c in (0, 1, 2)]
+    assert sizes[0] > 0 and sizes[1] > 0 and sizes[2] >= 0
+    nb = 4096 // 128
+    # the selection workspace holds at least the pooled map of every head
+    assert sizes[1] >= 2 * 4 * nb * (nb + 1) // 2 * 4
+    assert crisp.max_blocks(sh) == 2 * 4 * nb * (nb + 1) // 2
+    n = ctypes.c_size_t(0)
+    assert lib.crisp_workspace_bytes(ctypes.byref(sh), ctypes.byref(cfg), 9, ctypes.byref(n)) == PARAM
+    assert lib.crisp_workspace_bytes(ctypes.byref(sh), ctypes.byref(cfg), 0, None) == NULL
+    assert crisp.workspace_bytes(shape(batch=0), cfg, 1) == 0
+
+
+def _route(lib, sh, cfg, ptrs, ws_bytes):
+    q, k, c, p, pv, ps, ws = ptrs
+    return lib.crisp_route(ctypes.byref(sh), ctypes.byref(cfg), q, k, c, p, pv, ps, ws, ws_bytes, None)
+
+
+def test_route_rejects_before_any_hip_call(lib):
+    sh, cfg = shape(), crisp.config()
+    need = crisp.workspace_bytes(sh, cfg, 0)
+    good = [FAKE] * 7
+    assert _route(lib, sh, cfg, [FAKE, None] + good[2:], need) == NULL
+    assert _route(lib, sh, cfg, [FAKE + 8] + good[1:], need) == ALIGN
+    assert _route(lib, sh, cfg, good, need - 1) == WS
+    assert _route(lib, shape(n=100), cfg, good, need) == SHAPE
+    assert _route(lib, sh, crisp.config(block=256), good, need) == UNSUP
+    assert lib.crisp_route(None, ctypes.byref(cfg), *good, need, None) == NULL
+    # an empty batch enqueues nothing, whatever the pointers
+    assert _route(lib, shape(batch=0), cfg, [None] * 7, 0) == OK
+
+
+def test_select_rejects_before_any_hip_call(lib):
+    sh, cfg = shape(), crisp.config()
+    need = crisp.workspace_bytes(sh, cfg, 1)
+    cap = crisp.max_blocks(sh)
+
+    def call(cap_, ws_bytes, mask=None, rp=FAKE):
+        return lib.crisp_select(ctypes.byref(sh), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, rp, FAKE,
+                                cap_, mask, FAKE, ws_bytes, None)
+    assert call(cap - 1, need) == CAP
+    assert call(cap, need - 1) == WS
+    assert call(cap, need, mask=FAKE + 4) == ALIGN
+    assert call(cap, need, rp=None) == NULL
+
+
+def test_attention_rejects_before_any_hip_call(lib):
+    sh, cfg = shape(), crisp.config()
+    a = lib.crisp_sparse_attn(ctypes.byref(sh), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 2,
+                              None, 0, None)
+    assert a == PARAM
+    a = lib.crisp_sparse_attn(ctypes.byref(sh), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, None, 10, FAKE, 0,
+                              None, 0, None)
+    assert a == NULL
+    a = lib.crisp_sparse_attn(ctypes.byref(sh), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 0,
+                              None, 0, None)
+    assert a == PARAM
+    assert lib.dense_attn(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE + 2, 0, None) == ALIGN
+    assert lib.dense_attn(ctypes.byref(sh), FAKE, None, FAKE, FAKE, 0, None) == NULL
+    assert lib.dense_attn(ctypes.byref(shape(d=32)), FAKE, FAKE, FAKE, FAKE, 0, None) == SHAPE
+
+
+def test_status_strings(lib):
+    for st in (OK, NULL, SHAPE, PARAM, UNSUP, WS, CAP, HIP, ALIGN, 123):
+        assert lib.crisp_status_string(st)
+    assert lib.crisp_last_error() == b""
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(crisp, "_lib", None)
+    monkeypatch.setattr(crisp, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(crisp.CrispError):
+        crisp.load()
