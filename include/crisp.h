@@ -82,7 +82,7 @@ enum crisp_status {
 
 enum crisp_out_dtype { CRISP_OUT_F32 = 0, CRISP_OUT_BF16 = 1 };
 
-enum crisp_call { CRISP_CALL_ROUTE = 0, CRISP_CALL_SELECT = 1, CRISP_CALL_ATTN = 2 };
+enum crisp_call { CRISP_CALL_ROUTE = 0, CRISP_CALL_SELECT = 1, CRISP_CALL_ATTN = 2, CRISP_CALL_DENSE = 3 };
 
 /* Device workspace in bytes that `call` needs for this shape (pure host
  * arithmetic, no HIP call).  Writes *bytes; returns a status.  The workspace
@@ -149,7 +149,8 @@ int crisp_select(const crisp_shape* shape, const crisp_cfg* cfg,
  * out: [batch][h_q][n][d], f32 (CRISP_OUT_F32) or bf16 (CRISP_OUT_BF16).
  * bf16 MFMA for QK^T and PV with fp32 accumulation; softmax in fp32 with P
  * rounded to bf16 for the PV product.
- * ws: crisp_workspace_bytes(CRISP_CALL_ATTN) bytes. */
+ * ws: crisp_workspace_bytes(CRISP_CALL_ATTN) bytes (work-queue counters; the
+ * call resets them, so concurrent calls must not share one workspace). */
 int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg,
                       const void* q_bf16, const void* k_bf16, const void* v_bf16,
                       const int64_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
@@ -157,9 +158,11 @@ int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg,
 
 /* Dense exact causal attention (the result FlashAttention computes; digest,
  * prerequisite section on FlashAttention): crisp_sparse_attn with every key
- * block kb <= qb selected, same kernels and precision, no workspace. */
+ * block kb <= qb selected, same kernels and precision.
+ * ws: crisp_workspace_bytes(CRISP_CALL_DENSE) bytes (a few counters). */
 int dense_attn(const crisp_shape* shape, const void* q_bf16, const void* k_bf16,
-               const void* v_bf16, void* out, int out_dtype, void* stream);
+               const void* v_bf16, void* out, int out_dtype, void* ws, size_t ws_bytes,
+               void* stream);
 
 /* Static description of a status code. */
 const char* crisp_status_string(int status);

@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcrisp.so")
 _lib = None
 
-CALL_ROUTE, CALL_SELECT, CALL_ATTN = 0, 1, 2
+CALL_ROUTE, CALL_SELECT, CALL_ATTN, CALL_DENSE = 0, 1, 2, 3
 OUT_F32, OUT_BF16 = 0, 1
 
 
@@ -67,7 +67,7 @@ def load():
     lib.crisp_route.argtypes = [ps, pc, P, P, P, P, P, P, P, SZ, P]
     lib.crisp_select.argtypes = [ps, pc, P, P, P, P, P, P, P, I64, P, P, SZ, P]
     lib.crisp_sparse_attn.argtypes = [ps, pc, P, P, P, P, P, I64, P, I, P, SZ, P]
-    lib.dense_attn.argtypes = [ps, P, P, P, P, I, P]
+    lib.dense_attn.argtypes = [ps, P, P, P, P, I, P, SZ, P]
     lib.crisp_status_string.argtypes = [I]
     lib.crisp_status_string.restype = ctypes.c_char_p
     lib.crisp_last_error.restype = ctypes.c_char_p
@@ -196,14 +196,14 @@ def sparse_attn(q, k, v, sel: dict, cfg: Cfg | None = None, out=None, out_dtype=
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     nws = workspace_bytes(sh, cfg, CALL_ATTN)
-    ws = _workspace(nws, q.device, ws) if nws else None
+    ws = _workspace(nws, q.device, ws)
     _check(load().crisp_sparse_attn(ctypes.byref(sh), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(sel["row_ptr"]), _ptr(sel["col_idx"]), sel["col_idx"].numel(),
                                     _ptr(out), code, _ptr(ws), nws, _stream(stream)))
     return out
 
 
-def dense_attn(q, k, v, out=None, out_dtype=None, stream=None):
+def dense_attn(q, k, v, out=None, out_dtype=None, ws=None, stream=None):
     """Exact causal attention over every block (the dense baseline)."""
     import torch
     _check_qkv(q, k, v)
@@ -212,7 +212,10 @@ def dense_attn(q, k, v, out=None, out_dtype=None, stream=None):
     code = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    _check(load().dense_attn(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(out), code, _stream(stream)))
+    nws = workspace_bytes(sh, config(), CALL_DENSE)
+    ws = _workspace(nws, q.device, ws)
+    _check(load().dense_attn(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(out), code, _ptr(ws), nws,
+                             _stream(stream)))
     return out
 
 

@@ -24,6 +24,7 @@ namespace crisp {
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int NXCD = 8;   // accelerator complex dies of an MI355X
 
 template <int D>
 struct VTile {
@@ -75,19 +76,53 @@ __device__ __forceinline__ void store_vt_lds(uint16_t* __restrict__ vlds, const 
   }
 }
 
+// Work queues.  Items are (head, query block) rows.  Queue x (one per XCD;
+// workgroup i serves queue i % 8, and workgroups are dispatched to XCDs
+// round-robin) holds the chunks c = x, x+8, x+16, ... of QC consecutive query
+// blocks counted from the last one (longest causal rows first); inside a
+// chunk the items run head by head, so the CUs of an XCD work on adjacent
+// query blocks of one head at once and share its K/V tiles in their L2.
+// Workgroups take items from the queue's counter until it runs dry, so the
+// work balances whatever the heads' routes and row lengths.
+struct Queue {
+  int nb, qc;              // query blocks per head; chunk length
+  int64_t bh_total;        // batch * h_q
+  int64_t per_queue;       // items per queue
+};
+
+__host__ __device__ inline int queue_chunk(int nb) {
+  int qc = nb / 32;
+  return qc < 1 ? 1 : (qc > 32 ? 32 : qc);
+}
+
+__host__ inline Queue make_queue(int nb, int64_t bh_total) {
+  Queue qd;
+  qd.nb = nb;
+  qd.qc = queue_chunk(nb);
+  qd.bh_total = bh_total;
+  const int64_t chunks = (nb + qd.qc - 1) / qd.qc;
+  qd.per_queue = (chunks + NXCD - 1) / NXCD * bh_total * qd.qc;
+  return qd;
+}
+
+// Item u of queue x -> (query block, head row); false for the padding past the last block.
+__device__ __forceinline__ bool queue_item(const Queue& qd, int x, int64_t u, int& qb, int64_t& bh) {
+  const int64_t span = qd.bh_total * qd.qc;
+  const int64_t j = u / span, rem = u % span;
+  bh = rem / qd.qc;
+  const int64_t qtop = (j * NXCD + x) * qd.qc + rem % qd.qc;
+  if (qtop >= qd.nb) return false;
+  qb = qd.nb - 1 - (int)qtop;
+  return true;
+}
+
 template <int D, bool DENSE, bool OUT_BF16>
-__global__ __launch_bounds__(NTHR) void attn_kernel(
+__device__ __forceinline__ void attn_row(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_cap,
-    void* __restrict__ out, int n, int h_q, int group, int64_t bh_total, float c2) {
-  __shared__ __align__(16) uint16_t klds[Tile<D>::KLDS];
-  __shared__ __align__(16) uint16_t vlds[VTile<D>::VLDS];
+    void* __restrict__ out, int n, int h_q, int group, int qb, int64_t bh, float c2,
+    uint16_t* __restrict__ klds, uint16_t* __restrict__ vlds) {
   const int nb = n / BLK;
-  // Longest rows first: causal rows grow with the query block, so walk query
-  // blocks from the last one down, all heads of one query block together.
-  const int64_t wk = blockIdx.x;
-  const int qb = nb - 1 - (int)(wk / bh_total);
-  const int64_t bh = wk % bh_total;
   const int b = (int)(bh / h_q), h = (int)(bh % h_q);
   const int h_kv = h_q / group, g = h / group;
   const uint16_t* qh = q + (size_t)bh * n * D;
@@ -222,18 +257,61 @@ __global__ __launch_bounds__(NTHR) void attn_kernel(
     }
 }
 
+template <int D, bool DENSE, bool OUT_BF16>
+__global__ __launch_bounds__(NTHR) void attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_cap,
+    void* __restrict__ out, int n, int h_q, int group, Queue qd, int* __restrict__ counters, float c2) {
+  __shared__ __align__(16) uint16_t klds[Tile<D>::KLDS];
+  __shared__ __align__(16) uint16_t vlds[VTile<D>::VLDS];
+  __shared__ int64_t item;
+  const int x = (int)(blockIdx.x % NXCD);
+  for (;;) {
+    if (threadIdx.x == 0) item = atomicAdd(&counters[x], 1);
+    __syncthreads();
+    const int64_t u = item;
+    __syncthreads();
+    if (u >= qd.per_queue) break;
+    int qb;
+    int64_t bh;
+    if (!queue_item(qd, x, u, qb, bh)) continue;
+    attn_row<D, DENSE, OUT_BF16>(q, k, v, row_ptr, col_idx, col_cap, out, n, h_q, group, qb, bh, c2, klds, vlds);
+  }
+}
+
+__global__ void zero_counters_kernel(int* __restrict__ c) {
+  if (threadIdx.x < NXCD) c[threadIdx.x] = 0;
+}
+
+int workgroup_slots() {
+  static int slots = 0;
+  if (!slots) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    slots = cus;   // one attention workgroup fits per CU (register file and LDS)
+  }
+  return slots;
+}
+
 template <int D, bool DENSE>
 hipError_t attn_launch(const Dims& dm, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const int64_t* row_ptr, const int32_t* col_idx, int64_t cap, void* out,
-                       int out_bf16, hipStream_t st) {
+                       int out_bf16, int* counters, hipStream_t st) {
   const float c2 = LOG2E / sqrtf((float)D);
-  const int64_t nwork = dm.bh * dm.nb;
+  const Queue qd = make_queue(dm.nb, dm.bh);
+  int slots = workgroup_slots();
+  slots = (slots + NXCD - 1) / NXCD * NXCD;
+  const int64_t items = qd.per_queue * NXCD;
+  const unsigned grid = (unsigned)(items < slots ? (items + NXCD - 1) / NXCD * NXCD : slots);
+  zero_counters_kernel<<<1, 64, 0, st>>>(counters);
   if (out_bf16)
-    attn_kernel<D, DENSE, true><<<(unsigned)nwork, NTHR, 0, st>>>(q, k, v, row_ptr, col_idx, cap, out, dm.n,
-                                                                   dm.h_q, dm.group, dm.bh, c2);
+    attn_kernel<D, DENSE, true><<<grid, NTHR, 0, st>>>(q, k, v, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
+                                                       dm.group, qd, counters, c2);
   else
-    attn_kernel<D, DENSE, false><<<(unsigned)nwork, NTHR, 0, st>>>(q, k, v, row_ptr, col_idx, cap, out, dm.n,
-                                                                    dm.h_q, dm.group, dm.bh, c2);
+    attn_kernel<D, DENSE, false><<<grid, NTHR, 0, st>>>(q, k, v, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
+                                                        dm.group, qd, counters, c2);
   return hipGetLastError();
 }
 
@@ -241,15 +319,20 @@ hipError_t attn_launch(const Dims& dm, const uint16_t* q, const uint16_t* k, con
 
 hipError_t launch_sparse_attn(const Dims& dm, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int64_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
-                              void* out, int out_bf16, hipStream_t st) {
-  if (dm.d == 128) return attn_launch<128, false>(dm, q, k, v, row_ptr, col_idx, col_capacity, out, out_bf16, st);
-  return attn_launch<64, false>(dm, q, k, v, row_ptr, col_idx, col_capacity, out, out_bf16, st);
+                              void* out, int out_bf16, void* ws, hipStream_t st) {
+  int* counters = static_cast<int*>(ws);
+  if (dm.d == 128)
+    return attn_launch<128, false>(dm, q, k, v, row_ptr, col_idx, col_capacity, out, out_bf16, counters, st);
+  return attn_launch<64, false>(dm, q, k, v, row_ptr, col_idx, col_capacity, out, out_bf16, counters, st);
 }
 
 hipError_t launch_dense_attn(const Dims& dm, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             void* out, int out_bf16, hipStream_t st) {
-  if (dm.d == 128) return attn_launch<128, true>(dm, q, k, v, nullptr, nullptr, 0, out, out_bf16, st);
-  return attn_launch<64, true>(dm, q, k, v, nullptr, nullptr, 0, out, out_bf16, st);
+                             void* out, int out_bf16, void* ws, hipStream_t st) {
+  int* counters = static_cast<int*>(ws);
+  if (dm.d == 128) return attn_launch<128, true>(dm, q, k, v, nullptr, nullptr, 0, out, out_bf16, counters, st);
+  return attn_launch<64, true>(dm, q, k, v, nullptr, nullptr, 0, out, out_bf16, counters, st);
 }
+
+size_t attn_ws_bytes() { return 256; }
 
 }  // namespace crisp

@@ -82,7 +82,8 @@ size_t ws_bytes_for(const Dims& dm, int call) {
   switch (call) {
     case CRISP_CALL_ROUTE: return route_ws_layout(dm, nullptr, nullptr);
     case CRISP_CALL_SELECT: return crisp::select_ws_layout(dm, nullptr, nullptr);
-    case CRISP_CALL_ATTN: return 0;
+    case CRISP_CALL_ATTN: return crisp::attn_ws_bytes();
+    case CRISP_CALL_DENSE: return crisp::attn_ws_bytes();
     default: return (size_t)-1;
   }
 }
@@ -172,30 +173,32 @@ int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg, const void
   if (dm.batch == 0) return CRISP_OK;
   if (!q_bf16 || !k_bf16 || !v_bf16 || !row_ptr || !out) return CRISP_ERR_NULL;
   if (col_capacity > 0 && !col_idx) return CRISP_ERR_NULL;
+  if (!ws) return CRISP_ERR_NULL;
   if (misaligned(q_bf16) || misaligned(k_bf16) || misaligned(v_bf16) || misaligned(row_ptr) ||
-      (col_idx && misaligned(col_idx)) || misaligned(out) || (ws && misaligned(ws)))
+      (col_idx && misaligned(col_idx)) || misaligned(out) || misaligned(ws))
     return CRISP_ERR_ALIGN;
   if (ws_bytes < ws_bytes_for(dm, CRISP_CALL_ATTN)) return CRISP_ERR_WORKSPACE;
-  (void)ws;
   return hip_status(crisp::launch_sparse_attn(dm, static_cast<const uint16_t*>(q_bf16),
                                               static_cast<const uint16_t*>(k_bf16),
                                               static_cast<const uint16_t*>(v_bf16), row_ptr, col_idx, col_capacity,
-                                              out, out_dtype == CRISP_OUT_BF16, static_cast<hipStream_t>(stream)));
+                                              out, out_dtype == CRISP_OUT_BF16, ws, static_cast<hipStream_t>(stream)));
 }
 
 int dense_attn(const crisp_shape* shape, const void* q_bf16, const void* k_bf16, const void* v_bf16, void* out,
-               int out_dtype, void* stream) {
+               int out_dtype, void* ws, size_t ws_bytes, void* stream) {
   Dims dm;
   const int st = make_dims(shape, &dm);
   if (st) return st;
   if (out_dtype != CRISP_OUT_F32 && out_dtype != CRISP_OUT_BF16) return CRISP_ERR_PARAM;
   if (dm.batch == 0) return CRISP_OK;
-  if (!q_bf16 || !k_bf16 || !v_bf16 || !out) return CRISP_ERR_NULL;
-  if (misaligned(q_bf16) || misaligned(k_bf16) || misaligned(v_bf16) || misaligned(out)) return CRISP_ERR_ALIGN;
+  if (!q_bf16 || !k_bf16 || !v_bf16 || !out || !ws) return CRISP_ERR_NULL;
+  if (misaligned(q_bf16) || misaligned(k_bf16) || misaligned(v_bf16) || misaligned(out) || misaligned(ws))
+    return CRISP_ERR_ALIGN;
+  if (ws_bytes < ws_bytes_for(dm, CRISP_CALL_DENSE)) return CRISP_ERR_WORKSPACE;
   return hip_status(crisp::launch_dense_attn(dm, static_cast<const uint16_t*>(q_bf16),
                                              static_cast<const uint16_t*>(k_bf16),
                                              static_cast<const uint16_t*>(v_bf16), out,
-                                             out_dtype == CRISP_OUT_BF16, static_cast<hipStream_t>(stream)));
+                                             out_dtype == CRISP_OUT_BF16, ws, static_cast<hipStream_t>(stream)));
 }
 
 const char* crisp_status_string(int status) {

@@ -40,13 +40,13 @@ __device__ __forceinline__ int key_of_reg(int r, int lane) {
   return 16 * (r >> 3) + 8 * (lane >> 5) + (r & 7);
 }
 
-// float -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// Two floats -> packed bf16 pair (low half = lo), one v_cvt_pk_bf16_f32
+// (round to nearest even under the default rounding mode).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 

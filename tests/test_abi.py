@@ -71,8 +71,8 @@ def test_cfg_validation(lib, kw, status):
 def test_workspace_and_capacity_queries(lib):
     sh = shape(batch=2, n=4096, h_q=4, h_kv=2, d=128)
     cfg = crisp.config()
-    sizes = [crisp.workspace_bytes(sh, cfg, c) for c in (0, 1, 2)]
-    assert sizes[0] > 0 and sizes[1] > 0 and sizes[2] >= 0
+    sizes = [crisp.workspace_bytes(sh, cfg, c) for c in (0, 1, 2, 3)]
+    assert all(x > 0 for x in sizes)
     nb = 4096 // 128
     # the selection workspace holds at least the pooled map of every head
     assert sizes[1] >= 2 * 4 * nb * (nb + 1) // 2 * 4
@@ -118,18 +118,27 @@ def test_select_rejects_before_any_hip_call(lib):
 
 def test_attention_rejects_before_any_hip_call(lib):
     sh, cfg = shape(), crisp.config()
-    a = lib.crisp_sparse_attn(ctypes.byref(sh), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 2,
-                              None, 0, None)
-    assert a == PARAM
-    a = lib.crisp_sparse_attn(ctypes.byref(sh), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, None, 10, FAKE, 0,
-                              None, 0, None)
-    assert a == NULL
-    a = lib.crisp_sparse_attn(ctypes.byref(sh), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 0,
-                              None, 0, None)
-    assert a == PARAM
-    assert lib.dense_attn(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE + 2, 0, None) == ALIGN
-    assert lib.dense_attn(ctypes.byref(sh), FAKE, None, FAKE, FAKE, 0, None) == NULL
-    assert lib.dense_attn(ctypes.byref(shape(d=32)), FAKE, FAKE, FAKE, FAKE, 0, None) == SHAPE
+    need = crisp.workspace_bytes(sh, cfg, 2)
+    dneed = crisp.workspace_bytes(sh, cfg, 3)
+    assert need > 0 and dneed > 0
+
+    def sp(ws, ws_bytes, dtype=0, col=FAKE, cap=10):
+        return lib.crisp_sparse_attn(ctypes.byref(sh), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, col, cap, FAKE,
+                                     dtype, ws, ws_bytes, None)
+    assert sp(FAKE, need, dtype=2) == PARAM
+    assert sp(FAKE, need, col=None) == NULL
+    assert sp(FAKE, need, cap=-1) == PARAM
+    assert sp(None, need) == NULL
+    assert sp(FAKE, need - 1) == WS
+    assert sp(FAKE + 4, need) == ALIGN
+
+    def dn(q=FAKE, out=FAKE, ws=FAKE, ws_bytes=dneed, s=sh):
+        return lib.dense_attn(ctypes.byref(s), q, FAKE, FAKE, out, 0, ws, ws_bytes, None)
+    assert dn(out=FAKE + 2) == ALIGN
+    assert dn(q=None) == NULL
+    assert dn(ws=None) == NULL
+    assert dn(ws_bytes=dneed - 1) == WS
+    assert dn(s=shape(d=32)) == SHAPE
 
 
 def test_status_strings(lib):
