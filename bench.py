@@ -225,12 +225,14 @@ def main():
     import torch
     if args.copy_calibration:
         nbytes = args.copy_calibration << 20
+        # an elementwise kernel that reads nbytes and writes nbytes (dst = src + 1)
         src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.add(src, 1, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 3}))
+        print(json.dumps({"copy_kernel": "torch.add(uint8, 1)", "read_bytes_per_launch": nbytes,
+                          "write_bytes_per_launch": nbytes, "launches": 3}))
         return
 
     idx = ALIASES.get(args.workload) or int(args.workload)
