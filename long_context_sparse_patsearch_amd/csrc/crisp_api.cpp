@@ -82,8 +82,8 @@ size_t ws_bytes_for(const Dims& dm, int call) {
   switch (call) {
     case CRISP_CALL_ROUTE: return route_ws_layout(dm, nullptr, nullptr);
     case CRISP_CALL_SELECT: return crisp::select_ws_layout(dm, nullptr, nullptr);
-    case CRISP_CALL_ATTN: return crisp::attn_ws_bytes();
-    case CRISP_CALL_DENSE: return crisp::attn_ws_bytes();
+    case CRISP_CALL_ATTN: return crisp::attn_ws_bytes(dm);
+    case CRISP_CALL_DENSE: return crisp::attn_ws_bytes(dm);
     default: return (size_t)-1;
   }
 }

@@ -45,8 +45,8 @@ hipError_t launch_select(const Dims& dm, float alpha, float gamma, int kmin_bloc
                          int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st);
 
 // ---- attention (attn.hip) ----
-// ws: attn_ws_bytes() bytes of scratch (the work-queue counters)
-size_t attn_ws_bytes();
+// ws: attn_ws_bytes(dm) bytes of scratch (work-queue counters and a V^T copy)
+size_t attn_ws_bytes(const Dims& dm);
 hipError_t launch_sparse_attn(const Dims& dm, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int64_t* row_ptr, const int32_t* col_idx,
                               int64_t col_capacity, void* out, int out_bf16, void* ws, hipStream_t st);
