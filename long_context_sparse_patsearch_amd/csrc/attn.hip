@@ -55,6 +55,16 @@ __device__ __forceinline__ int swz(int row, int c) {
   else return c ^ ((row >> 1) & 7);
 }
 
+// One direct global->LDS load of 16 bytes per lane: lane i writes LDS bytes
+// [lds_off + 16 i, lds_off + 16 i + 16).  Issued as asm so that the compiler does
+// not treat the other LDS buffer as aliased and wait for these loads before
+// every LDS read; the kernel waits for them itself (vm_wait) before the barrier
+// that publishes a stage.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_off) : "memory", "m0");
+}
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Work queues.  Items are (head, query block) rows.  Queue x (one per XCD;
 // workgroup i serves queue i % 8, and workgroups are dispatched to XCDs
 // round-robin) holds the chunks c = x, x+8, x+16, ... of QC consecutive query
@@ -66,7 +76,7 @@ __device__ __forceinline__ int swz(int row, int c) {
 struct Queue {
   int nb, qc;              // query blocks per head; chunk length
   int64_t bh_total;        // batch * h_q
-  int64_t per_queue;       // items per queue
+  int per_queue;           // items per queue
 };
 
 inline int queue_chunk(int nb) {
@@ -80,12 +90,12 @@ inline Queue make_queue(int nb, int64_t bh_total) {
   qd.qc = queue_chunk(nb);
   qd.bh_total = bh_total;
   const int64_t chunks = (nb + qd.qc - 1) / qd.qc;
-  qd.per_queue = (chunks + NXCD - 1) / NXCD * bh_total * qd.qc;
+  qd.per_queue = (int)((chunks + NXCD - 1) / NXCD * bh_total * qd.qc);
   return qd;
 }
 
 // Item u of queue x -> (query block, head row); false for the padding past the last block.
-__device__ __forceinline__ bool queue_item(const Queue& qd, int x, int64_t u, int& qb, int64_t& bh) {
+__device__ __forceinline__ bool queue_item(const Queue& qd, int x, int u, int& qb, int64_t& bh) {
   const int64_t span = qd.bh_total * qd.qc;
   const int64_t j = u / span, rem = u % span;
   bh = rem / qd.qc;
@@ -102,7 +112,7 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
     void* __restrict__ out, int n, int h_q, int group, Queue qd, int* __restrict__ counters, float c2) {
   using S = Stage<D>;
   __shared__ __align__(16) char lds[2 * S::BYTES];
-  __shared__ int64_t item;
+  __shared__ int item;
   const int x = (int)(blockIdx.x % NXCD);
   const int w = wave_id(), lane = lane_id();
   const int hi = lane >> 5;
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
   for (;;) {
     if (threadIdx.x == 0) item = atomicAdd(&counters[x], 1);
     __syncthreads();
-    const int64_t u = item;
+    const int u = __builtin_amdgcn_readfirstlane(item);
     __syncthreads();
     if (u >= qd.per_queue) break;
     int qb;
@@ -141,7 +151,7 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
       t0 = t0 < 0 ? 0 : (t0 > col_cap ? col_cap : t0);
       t1 = t1 < t0 ? t0 : (t1 > col_cap ? col_cap : t1);
     }
-    auto kb_at = [&](int64_t t) -> int { return DENSE ? (int)t : __builtin_amdgcn_readfirstlane(col_idx[t]); };
+    auto kb_at = [&](int64_t t) -> int { return DENSE ? (int)t : col_idx[t]; };
     auto next_valid = [&](int64_t t) -> int64_t {
       if (DENSE) return t;
       while (t < t1) {
@@ -153,25 +163,27 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
     };
 
     // issue the direct loads of stage (block kb, half hf) into buffer bf
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)lds);
+    const uint32_t wslot = (uint32_t)__builtin_amdgcn_readfirstlane(w) * 64u;
     auto issue = [&](int kb, int hf, int bf) {
-      char* kbuf = lds + bf * S::BYTES;
-      char* vbuf = kbuf + S::KBYTES;
+      const uint32_t kbuf = lds0 + bf * S::BYTES;
+      const uint32_t vbuf = kbuf + S::KBYTES;
       const int key0 = kb * BLK + hf * KS;
 #pragma unroll
       for (int i = 0; i < S::KLOADS; ++i) {
-        const int slot = (i * 4 + w) * 64;
-        const int p = slot + lane;
+        const uint32_t slot = i * 4 * 64 + wslot;
+        const int p = (int)slot + lane;
         const int row = p / S::KCPR;
         const int c = swz<S::KCPR>(row, p % S::KCPR);
-        __builtin_amdgcn_global_load_lds(kg + (size_t)(key0 + row) * D + c * 8, kbuf + slot * 16, 16, 0, 0);
+        dma16(kg + (size_t)(key0 + row) * D + c * 8, kbuf + slot * 16);
       }
 #pragma unroll
       for (int i = 0; i < S::VLOADS; ++i) {
-        const int slot = (i * 4 + w) * 64;
-        const int p = slot + lane;
+        const uint32_t slot = i * 4 * 64 + wslot;
+        const int p = (int)slot + lane;
         const int row = p / S::VCPR;
         const int c = swz<S::VCPR>(row, p % S::VCPR);
-        __builtin_amdgcn_global_load_lds(vtg + (size_t)row * n + key0 + c * 8, vbuf + slot * 16, 16, 0, 0);
+        dma16(vtg + (size_t)row * n + key0 + c * 8, vbuf + slot * 16);
       }
     };
 
@@ -180,28 +192,41 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
       const uint16_t* qp = q + ((size_t)bh * n + (size_t)qb * BLK + qloc) * D + 8 * hi;
 #pragma unroll
       for (int s = 0; s < S::NSTEP; ++s) qf[s] = as_bf16x8(ld16(qp + 16 * s));
+      // consume the query loads here (an empty asm reading the registers), so
+      // that the compiler completes them before the stage loop and places no
+      // vector-memory waits inside it
+      if constexpr (S::NSTEP == 8)
+        asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]), "v"(qf[7]));
+      else
+        asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]));
     }
     f32x16 o[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
     float m = M_INIT, l = 0.f;
 
+    // stage sequence: (block kb, half 0), (kb, 1), (next block, 0), ...; the next
+    // entry of the row is fetched one stage before it is needed and validated
+    // only then (entries outside [0, qb] are skipped)
     int64_t t = next_valid(t0);
     int kb = t < t1 ? kb_at(t) : 0;
+    int64_t tn = t + 1;
+    int kbn = tn < t1 ? kb_at(tn) : -1;
     int hf = 0, bf = 0;
     if (t < t1) issue(kb, 0, 0);
     while (t < t1) {
-      // next stage: second half of this block, or the first half of the next selected block
-      int64_t tn = t;
-      int kbn = kb, hfn = hf + 1;
-      if (hfn == 2) {
-        hfn = 0;
-        tn = next_valid(t + 1);
-        kbn = tn < t1 ? kb_at(tn) : 0;
-      }
-      __builtin_amdgcn_s_waitcnt(0);
+      vm_wait();
       __syncthreads();
-      if (tn < t1) issue(kbn, hfn, bf ^ 1);
+      // stage after this one: the second half of kb, or the first half of the next entry
+      if (hf == 0) {
+        issue(kb, 1, bf ^ 1);
+      } else {
+        if (!DENSE && tn < t1 && (kbn < 0 || kbn > qb)) {
+          tn = next_valid(tn + 1);
+          kbn = tn < t1 ? kb_at(tn) : -1;
+        }
+        if (tn < t1) issue(kbn, 0, bf ^ 1);
+      }
 
       const char* kbuf = lds + bf * S::BYTES;
       const char* vbuf = kbuf + S::KBYTES;
@@ -273,9 +298,15 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
           for (int cc = 0; cc < 4; ++cc)
             o[ds] = mfma_32x32x16(as_bf16x8(ld16(vr + 32 * ds * S::VROW + ((2 * cc + hi) ^ vfix) * 16)), pb[cc], o[ds]);
       }
-      t = tn;
-      kb = kbn;
-      hf = hfn;
+      if (hf == 0) {
+        hf = 1;
+      } else {
+        hf = 0;
+        t = tn;
+        kb = kbn;
+        tn = t + 1;
+        kbn = tn < t1 ? kb_at(tn) : -1;
+      }
       bf ^= 1;
     }
 
