@@ -63,6 +63,14 @@ __device__ __forceinline__ int swz(int row, int c) {
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_off) : "memory", "m0");
 }
+// The same with a scalar base address: lane i loads 16 bytes at gbase + voff_i
+// into LDS bytes [lds_base + IMM + 16 i, ...).
+template <uint32_t IMM>
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* gbase, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds_base),
+               "i"(IMM)
+               : "memory", "m0", "scc");
+}
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Work queues.  Items are (head, query block) rows.  Queue x (one per XCD;
@@ -125,6 +133,26 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
   const int kfix = (S::KCPR == 16) ? (krow & 15) : ((krow >> 1) & 7);
   const int vrow = lane & 31;                                  // + 32 ds
   const int vfix = (vrow >> 1) & 7;
+  static_assert(S::KLOADS == 2 || S::KLOADS == 4, "direct loads per stage");
+  static_assert(S::VLOADS == 2 || S::VLOADS == 4, "direct loads per stage");
+  // Direct-load byte offsets, the same for every stage.  Load i of wave w fills
+  // LDS chunks p = (4i + w)*64 + lane of a stage buffer with the (row, logical
+  // chunk) the swizzle maps there; the swizzle term does not depend on i (rows
+  // advance by a multiple of its period), so load i's offset is load 0's plus
+  // a fixed step (16 K rows, 32 V^T rows).
+  uint32_t kdma[S::KLOADS], vdma[S::VLOADS];
+  {
+    const int p = w * 64 + lane;
+    const int kr0 = p / S::KCPR, vr0 = p / S::VCPR;
+    const uint32_t k0 = (uint32_t)(kr0 * D + swz<S::KCPR>(kr0, p % S::KCPR) * 8) * 2u;
+    const uint32_t v0 = (uint32_t)(vr0 * n + swz<S::VCPR>(vr0, p % S::VCPR) * 8) * 2u;
+#pragma unroll
+    for (int i = 0; i < S::KLOADS; ++i) kdma[i] = k0 + i * (4 * 64 / S::KCPR * S::KROW);
+#pragma unroll
+    for (int i = 0; i < S::VLOADS; ++i) vdma[i] = v0 + (uint32_t)(i * (4 * 64 / S::VCPR)) * (uint32_t)n * 2u;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)lds);
+  const uint32_t lds0w = lds0 + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;   // this wave's first KiB
 
   for (;;) {
     if (threadIdx.x == 0) item = atomicAdd(&counters[x], 1);
@@ -163,27 +191,24 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
     };
 
     // issue the direct loads of stage (block kb, half hf) into buffer bf
-    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)lds);
-    const uint32_t wslot = (uint32_t)__builtin_amdgcn_readfirstlane(w) * 64u;
+    const char* kgb = reinterpret_cast<const char*>(kg);
+    const char* vgb = reinterpret_cast<const char*>(vtg);
     auto issue = [&](int kb, int hf, int bf) {
-      const uint32_t kbuf = lds0 + bf * S::BYTES;
-      const uint32_t vbuf = kbuf + S::KBYTES;
       const int key0 = kb * BLK + hf * KS;
-#pragma unroll
-      for (int i = 0; i < S::KLOADS; ++i) {
-        const uint32_t slot = i * 4 * 64 + wslot;
-        const int p = (int)slot + lane;
-        const int row = p / S::KCPR;
-        const int c = swz<S::KCPR>(row, p % S::KCPR);
-        dma16(kg + (size_t)(key0 + row) * D + c * 8, kbuf + slot * 16);
+      const char* gk = kgb + (size_t)key0 * D * 2;
+      const char* gv = vgb + (size_t)key0 * 2;
+      const uint32_t lk = lds0w + bf * S::BYTES, lv = lk + S::KBYTES;
+      dma16s<0>(kdma[0], gk, lk);
+      dma16s<4096>(kdma[1], gk, lk);
+      if constexpr (S::KLOADS > 2) {
+        dma16s<8192>(kdma[2], gk, lk);
+        dma16s<12288>(kdma[3], gk, lk);
       }
-#pragma unroll
-      for (int i = 0; i < S::VLOADS; ++i) {
-        const uint32_t slot = i * 4 * 64 + wslot;
-        const int p = (int)slot + lane;
-        const int row = p / S::VCPR;
-        const int c = swz<S::VCPR>(row, p % S::VCPR);
-        dma16(vtg + (size_t)row * n + key0 + c * 8, vbuf + slot * 16);
+      dma16s<0>(vdma[0], gv, lv);
+      dma16s<4096>(vdma[1], gv, lv);
+      if constexpr (S::VLOADS > 2) {
+        dma16s<8192>(vdma[2], gv, lv);
+        dma16s<12288>(vdma[3], gv, lv);
       }
     };
 
@@ -234,16 +259,14 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
       const int kloc0 = hf * KS;                 // first key of the stage inside the block
       // a wave whose queries all precede the stage has nothing to do in it
       if (!(diag && 32 * w + 31 < kloc0)) {
-        f32x16 s[2];
+        // the two 32-key accumulators alternate, so consecutive MFMAs are independent
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+        const char* kr = kbuf + krow * S::KROW;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          f32x16 acc = {};
-          const char* kr = kbuf + (32 * ks + krow) * S::KROW;
+        for (int st = 0; st < S::NSTEP; ++st)
 #pragma unroll
-          for (int st = 0; st < S::NSTEP; ++st)
-            acc = mfma_32x32x16(as_bf16x8(ld16(kr + ((2 * st + hi) ^ kfix) * 16)), qf[st], acc);
-          s[ks] = acc;
-        }
+          for (int ks = 0; ks < 2; ++ks)
+            s[ks] = mfma_32x32x16(as_bf16x8(ld16(kr + 32 * ks * S::KROW + ((2 * st + hi) ^ kfix) * 16)), qf[st], s[ks]);
         if (diag && 32 * w < kloc0 + KS - 1) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
@@ -270,32 +293,29 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
           m = mn;
         }
         const float nm = -m;
-        float ls = 0.f;
         bf16x8 pb[4];
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          float p[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            p[r] = fast_exp2(fmaf(s[ks][r], c2, nm));
-            ls += p[r];
-          }
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            uint4 uu;
-            uu.x = pack_bf16x2(p[8 * c + 0], p[8 * c + 1]);
-            uu.y = pack_bf16x2(p[8 * c + 2], p[8 * c + 3]);
-            uu.z = pack_bf16x2(p[8 * c + 4], p[8 * c + 5]);
-            uu.w = pack_bf16x2(p[8 * c + 6], p[8 * c + 7]);
-            pb[2 * ks + c] = as_bf16x8(uu);
+            uint32_t wv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float a0 = fast_exp2(fmaf(s[ks][8 * c + 2 * e], c2, nm));
+              const float a1 = fast_exp2(fmaf(s[ks][8 * c + 2 * e + 1], c2, nm));
+              wv[e] = pack_bf16x2(a0, a1);
+              // the row sum uses the rounded weights, the same ones the PV product uses
+              l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv[e]), one2, l, false);
+            }
+            pb[2 * ks + c] = as_bf16x8(make_uint4(wv[0], wv[1], wv[2], wv[3]));
           }
         }
-        l += ls;
         const char* vr = vbuf + vrow * S::VROW;
 #pragma unroll
-        for (int ds = 0; ds < D / 32; ++ds)
+        for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc)
+          for (int ds = 0; ds < D / 32; ++ds)
             o[ds] = mfma_32x32x16(as_bf16x8(ld16(vr + 32 * ds * S::VROW + ((2 * cc + hi) ^ vfix) * 16)), pb[cc], o[ds]);
       }
       if (hf == 0) {
