@@ -55,16 +55,11 @@ __device__ __forceinline__ int swz(int row, int c) {
   else return c ^ ((row >> 1) & 7);
 }
 
-// One direct global->LDS load of 16 bytes per lane: lane i writes LDS bytes
-// [lds_off + 16 i, lds_off + 16 i + 16).  Issued as asm so that the compiler does
-// not treat the other LDS buffer as aliased and wait for these loads before
-// every LDS read; the kernel waits for them itself (vm_wait) before the barrier
-// that publishes a stage.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_off) : "memory", "m0");
-}
-// The same with a scalar base address: lane i loads 16 bytes at gbase + voff_i
-// into LDS bytes [lds_base + IMM + 16 i, ...).
+// One direct global->LDS load of 16 bytes per lane: lane i loads 16 bytes at
+// gbase + voff_i into LDS bytes [lds_base + IMM + 16 i, ...).  Issued as asm so
+// that the compiler does not treat the other LDS buffers as aliased and wait
+// for these loads before every LDS read; the kernel waits for them itself
+// (vm_wait) before the barrier that publishes a stage.
 template <uint32_t IMM>
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* gbase, uint32_t lds_base) {
   asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds_base),
@@ -113,13 +108,127 @@ __device__ __forceinline__ bool queue_item(const Queue& qd, int x, int u, int& q
   return true;
 }
 
+// sched_group_barrier instruction classes
+constexpr int SG_VALU = 0x2, SG_MFMA = 0x8, SG_DSR = 0x100;
+constexpr int LDS_AHEAD = 6;             // operand reads kept in flight ahead of the MFMAs
+
+// Phase 1 of a stage: the next stage's scores S_n = K_n Q^T (when HAS_NEXT)
+// with the softmax weights of the current stage's scores s_c interleaved
+// between the MFMAs (two, or four for d = 64, weights per MFMA).  Weights
+// p = 2^(s c2 - m) are rounded to bf16 pairs for the PV product, and the row
+// sum l accumulates those rounded pairs.
+template <int D, bool HAS_NEXT>
+__device__ __forceinline__ void qk_softmax(const char* kbase, const uint32_t (&koff)[D / 16],
+                                           const bf16x8 (&qf)[D / 16], f32x16 (&sn)[2], const f32x16 (&sc)[2],
+                                           float c2, float nm, bf16x8 (&pb)[4], float& l) {
+  constexpr int NQK = D / 8;     // QK MFMAs per stage
+  constexpr int EPM = 32 / NQK;  // weights per MFMA
+  constexpr int KROW = D * 2;
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  uint32_t wv[16];
+  if (HAS_NEXT) {
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+  }
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    if (HAS_NEXT) {
+      const int st = i >> 1, ks = i & 1;
+      sn[ks] = mfma_32x32x16(as_bf16x8(ld16(kbase + koff[st] + 32 * ks * KROW)), qf[st], sn[ks]);
+    }
+#pragma unroll
+    for (int e = 0; e < EPM; e += 2) {
+      const int j = i * EPM + e, ks = j >> 4, r = j & 15;
+      const float a0 = fast_exp2(fmaf(sc[ks][r], c2, nm));
+      const float a1 = fast_exp2(fmaf(sc[ks][r + 1], c2, nm));
+      wv[j >> 1] = pack_bf16x2(a0, a1);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv[j >> 1]), one2, l, false);
+    }
+  }
+  if (HAS_NEXT) {
+    __builtin_amdgcn_sched_group_barrier(SG_DSR, LDS_AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 3 * EPM / 2, 0);
+      if (i + LDS_AHEAD < NQK) __builtin_amdgcn_sched_group_barrier(SG_DSR, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 3 * EPM / 2, 0);
+    }
+  }
+  // consume the weights and the row sum here (an empty asm reading them), so
+  // that the compiler computes them under this phase's MFMAs instead of
+  // sinking them into the PV phase
+  asm volatile("" ::"v"(wv[0]), "v"(wv[1]), "v"(wv[2]), "v"(wv[3]), "v"(wv[4]), "v"(wv[5]), "v"(wv[6]), "v"(wv[7]),
+               "v"(wv[8]), "v"(wv[9]), "v"(wv[10]), "v"(wv[11]), "v"(wv[12]), "v"(wv[13]), "v"(wv[14]), "v"(wv[15]),
+               "v"(l));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) pb[c] = as_bf16x8(make_uint4(wv[4 * c], wv[4 * c + 1], wv[4 * c + 2], wv[4 * c + 3]));
+}
+
+// Phase 2 of a stage: O^T += V^T P^T for the current stage, with the row
+// maximum of the next stage's scores (when HAS_NEXT) interleaved; returns it
+// (both lanes of a query column hold the same value).
+template <int D, bool HAS_NEXT>
+__device__ __forceinline__ float pv_max(const char* vbase, const uint32_t (&voff)[4], const bf16x8 (&pb)[4],
+                                        f32x16 (&o)[D / 32], const f32x16 (&sn)[2]) {
+  constexpr int VROW = KS * 2;
+  float t = -INFINITY;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+      o[ds] = mfma_32x32x16(as_bf16x8(ld16(vbase + voff[cc] + 32 * ds * VROW)), pb[cc], o[ds]);
+  if (HAS_NEXT) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t = fmaxf(t, sn[ks][r]);
+    t = fmaxf(t, xor_shfl(t, 32));
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_DSR, LDS_AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < 4 * (D / 32); ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    if (HAS_NEXT) __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
+    if (i + LDS_AHEAD < 4 * (D / 32)) __builtin_amdgcn_sched_group_barrier(SG_DSR, 1, 0);
+  }
+  return t;
+}
+
+// Causal mask of a stage of the diagonal block: keys after the lane's query go to -inf.
+// The threshold passes through an empty asm so that the compiler computes the
+// comparisons here instead of hoisting all of them out of the stage loop
+// (which would keep 32 lane masks live in scalar registers).
+__device__ __forceinline__ void mask_diag(f32x16 (&s)[2], int kloc0, int qloc, int lane) {
+  int lim = qloc - kloc0 - 8 * (lane >> 5);   // key_of_reg(r, lane) - 8 (lane >> 5) > lim  <=>  key > query
+  asm volatile("" : "+v"(lim));
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * ks + 16 * (r >> 3) + (r & 7) > lim) s[ks][r] = -INFINITY;
+}
+
+// Online-softmax bookkeeping for a stage whose score maximum (in score units) is t.
+__device__ __forceinline__ void update_max(float t, float c2, float& m, float& corr, bool& any) {
+  const float tmu = t * c2;
+  const bool need = tmu > m + RESCALE_LOG2;
+  any = __ballot(need) != 0;
+  const float mn = need ? tmu : m;
+  corr = fast_exp2(m - mn);
+  m = mn;
+}
+
 template <int D, bool DENSE, bool OUT_BF16>
 __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
     const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_cap,
     void* __restrict__ out, int n, int h_q, int group, Queue qd, int* __restrict__ counters, float c2) {
   using S = Stage<D>;
-  __shared__ __align__(16) char lds[2 * S::BYTES];
+  // LDS: K stage buffers 0 and 1 (first and second half of a block), then V^T
+  // stage buffers 0 and 1.  The V^T load runs one stage behind the K load, so
+  // the next stage's K and the current stage's V^T are resident together.
+  __shared__ __align__(16) char lds[2 * S::KBYTES + 2 * S::VBYTES];
   __shared__ int item;
   const int x = (int)(blockIdx.x % NXCD);
   const int w = wave_id(), lane = lane_id();
@@ -129,10 +238,21 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
   const int h_kv = h_q / group;
 
   // per-lane LDS read offsets, the same for every stage
-  const int krow = key_row_of_lane(lane & 31);                 // + 32 ks
-  const int kfix = (S::KCPR == 16) ? (krow & 15) : ((krow >> 1) & 7);
-  const int vrow = lane & 31;                                  // + 32 ds
-  const int vfix = (vrow >> 1) & 7;
+  uint32_t koff[S::NSTEP], voff[4];
+  {
+    const int krow = key_row_of_lane(lane & 31);   // + 32 ks
+    const int kfix = (S::KCPR == 16) ? (krow & 15) : ((krow >> 1) & 7);
+    const int vrow = lane & 31;                    // + 32 ds
+    const int vfix = (vrow >> 1) & 7;
+#pragma unroll
+    for (int st = 0; st < S::NSTEP; ++st) koff[st] = krow * S::KROW + (((2 * st + hi) ^ kfix) * 16);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) voff[cc] = vrow * S::VROW + (((2 * cc + hi) ^ vfix) * 16);
+  }
+  const char* kbuf0 = lds;
+  const char* kbuf1 = lds + S::KBYTES;
+  const char* vbuf0 = lds + 2 * S::KBYTES;
+  const char* vbuf1 = vbuf0 + S::VBYTES;
   static_assert(S::KLOADS == 2 || S::KLOADS == 4, "direct loads per stage");
   static_assert(S::VLOADS == 2 || S::VLOADS == 4, "direct loads per stage");
   // Direct-load byte offsets, the same for every stage.  Load i of wave w fills
@@ -152,7 +272,7 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
     for (int i = 0; i < S::VLOADS; ++i) vdma[i] = v0 + (uint32_t)(i * (4 * 64 / S::VCPR)) * (uint32_t)n * 2u;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)lds);
-  const uint32_t lds0w = lds0 + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;   // this wave's first KiB
+  const uint32_t lds0w = lds0 + (uint32_t)w * 1024u;   // this wave's first KiB of a buffer
 
   for (;;) {
     if (threadIdx.x == 0) item = atomicAdd(&counters[x], 1);
@@ -165,9 +285,33 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
     if (!queue_item(qd, x, u, qb, bh)) continue;
 
     const int b = (int)(bh / h_q), h = (int)(bh % h_q), g = h / group;
-    const uint16_t* kg = k + ((size_t)b * h_kv + g) * n * D;
-    const uint16_t* vtg = vt + ((size_t)b * h_kv + g) * (size_t)D * n;
+    const char* kgb = reinterpret_cast<const char*>(k + ((size_t)b * h_kv + g) * n * D);
+    const char* vgb = reinterpret_cast<const char*>(vt + ((size_t)b * h_kv + g) * (size_t)D * n);
+    auto issue_k = [&](int kb, int hf, uint32_t lbuf) {
+      const char* gb = kgb + (size_t)(kb * BLK + hf * KS) * D * 2;
+      const uint32_t lb = lds0w + lbuf;
+      dma16s<0>(kdma[0], gb, lb);
+      dma16s<4096>(kdma[1], gb, lb);
+      if constexpr (S::KLOADS > 2) {
+        dma16s<8192>(kdma[2], gb, lb);
+        dma16s<12288>(kdma[3], gb, lb);
+      }
+    };
+    auto issue_v = [&](int kb, int hf, uint32_t lbuf) {
+      const char* gb = vgb + (size_t)(kb * BLK + hf * KS) * 2;
+      const uint32_t lb = lds0w + lbuf;
+      dma16s<0>(vdma[0], gb, lb);
+      dma16s<4096>(vdma[1], gb, lb);
+      if constexpr (S::VLOADS > 2) {
+        dma16s<8192>(vdma[2], gb, lb);
+        dma16s<12288>(vdma[3], gb, lb);
+      }
+    };
+    constexpr uint32_t LK0 = 0, LK1 = S::KBYTES, LV0 = 2 * S::KBYTES, LV1 = 2 * S::KBYTES + S::VBYTES;
 
+    // Row entries: positions [t0, t1) of col_idx, read 64 at a time (one per
+    // lane) with a ballot of the valid ones (block index in [0, qb]); invalid
+    // entries are skipped.
     int64_t t0, t1;
     if (DENSE) {
       t0 = 0;
@@ -179,37 +323,26 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
       t0 = t0 < 0 ? 0 : (t0 > col_cap ? col_cap : t0);
       t1 = t1 < t0 ? t0 : (t1 > col_cap ? col_cap : t1);
     }
-    auto kb_at = [&](int64_t t) -> int { return DENSE ? (int)t : col_idx[t]; };
-    auto next_valid = [&](int64_t t) -> int64_t {
-      if (DENSE) return t;
-      while (t < t1) {
-        const int kb = kb_at(t);
-        if (kb >= 0 && kb <= qb) break;
-        ++t;
+    int64_t cb = -1;      // first position of the chunk held in cval
+    int cval = -1;
+    uint64_t cmask = 0;
+    auto next_valid = [&](int64_t p) -> int64_t {
+      if (DENSE) return p;
+      for (;;) {
+        if (p >= t1) return t1;
+        if (cb < 0 || p >= cb + 64) {
+          cb = p;
+          cval = (p + lane < t1) ? col_idx[p + lane] : -1;
+          cmask = __ballot(cval >= 0 && cval <= qb);
+        }
+        const uint64_t bits = cmask >> (int)(p - cb);
+        if (bits) return p + __builtin_ctzll(bits);
+        p = cb + 64;
       }
-      return t;
     };
-
-    // issue the direct loads of stage (block kb, half hf) into buffer bf
-    const char* kgb = reinterpret_cast<const char*>(kg);
-    const char* vgb = reinterpret_cast<const char*>(vtg);
-    auto issue = [&](int kb, int hf, int bf) {
-      const int key0 = kb * BLK + hf * KS;
-      const char* gk = kgb + (size_t)key0 * D * 2;
-      const char* gv = vgb + (size_t)key0 * 2;
-      const uint32_t lk = lds0w + bf * S::BYTES, lv = lk + S::KBYTES;
-      dma16s<0>(kdma[0], gk, lk);
-      dma16s<4096>(kdma[1], gk, lk);
-      if constexpr (S::KLOADS > 2) {
-        dma16s<8192>(kdma[2], gk, lk);
-        dma16s<12288>(kdma[3], gk, lk);
-      }
-      dma16s<0>(vdma[0], gv, lv);
-      dma16s<4096>(vdma[1], gv, lv);
-      if constexpr (S::VLOADS > 2) {
-        dma16s<8192>(vdma[2], gv, lv);
-        dma16s<12288>(vdma[3], gv, lv);
-      }
+    auto entry = [&](int64_t p) -> int {
+      if (DENSE) return (int)p;
+      return __builtin_amdgcn_readlane(cval, (int)(p - cb));
     };
 
     bf16x8 qf[S::NSTEP];
@@ -228,106 +361,83 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
     f32x16 o[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
-    float m = M_INIT, l = 0.f;
+    float m = M_INIT, l = 0.f, corr = 1.f;
+    bool any = false;
 
-    // stage sequence: (block kb, half 0), (kb, 1), (next block, 0), ...; the next
-    // entry of the row is fetched one stage before it is needed and validated
-    // only then (entries outside [0, qb] are skipped)
-    int64_t t = next_valid(t0);
-    int kb = t < t1 ? kb_at(t) : 0;
-    int64_t tn = t + 1;
-    int kbn = tn < t1 ? kb_at(tn) : -1;
-    int hf = 0, bf = 0;
-    if (t < t1) issue(kb, 0, 0);
-    while (t < t1) {
+    int64_t pc = next_valid(t0);
+    if (pc < t1) {
+      int kb = entry(pc);
+      int64_t pn = next_valid(pc + 1);
+      int kbn = pn < t1 ? entry(pn) : -1;
+      f32x16 sa[2], sb[2];
+      bf16x8 pb[4];
+      // prologue: the first half of the first block
+      issue_k(kb, 0, LK0);
       vm_wait();
       __syncthreads();
-      // stage after this one: the second half of kb, or the first half of the next entry
-      if (hf == 0) {
-        issue(kb, 1, bf ^ 1);
-      } else {
-        if (!DENSE && tn < t1 && (kbn < 0 || kbn > qb)) {
-          tn = next_valid(tn + 1);
-          kbn = tn < t1 ? kb_at(tn) : -1;
-        }
-        if (tn < t1) issue(kbn, 0, bf ^ 1);
-      }
-
-      const char* kbuf = lds + bf * S::BYTES;
-      const char* vbuf = kbuf + S::KBYTES;
-      const bool diag = (kb == qb);
-      const int kloc0 = hf * KS;                 // first key of the stage inside the block
-      // a wave whose queries all precede the stage has nothing to do in it
-      if (!(diag && 32 * w + 31 < kloc0)) {
-        // the two 32-key accumulators alternate, so consecutive MFMAs are independent
-        f32x16 s[2] = {f32x16{}, f32x16{}};
-        const char* kr = kbuf + krow * S::KROW;
+      issue_k(kb, 1, LK1);
+      issue_v(kb, 0, LV0);
+      sa[0] = f32x16{};
+      sa[1] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < S::NSTEP; ++st)
+      for (int st = 0; st < S::NSTEP; ++st)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            s[ks] = mfma_32x32x16(as_bf16x8(ld16(kr + 32 * ks * S::KROW + ((2 * st + hi) ^ kfix) * 16)), qf[st], s[ks]);
-        if (diag && 32 * w < kloc0 + KS - 1) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kloc0 + 32 * ks + key_of_reg(r, lane) > qloc) s[ks][r] = -INFINITY;
-        }
-        float tmax = s[0][0];
+        for (int ks = 0; ks < 2; ++ks)
+          sa[ks] = mfma_32x32x16(as_bf16x8(ld16(kbuf0 + koff[st] + 32 * ks * S::KROW)), qf[st], sa[ks]);
+      if (kb == qb) mask_diag(sa, 0, qloc, lane);
+      {
+        float t = -INFINITY;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[ks][r]);
-        tmax = fmaxf(tmax, xor_shfl(tmax, 32));
-        const float tmu = tmax * c2;
-        const bool need = tmu > m + RESCALE_LOG2;
-        if (__ballot(need)) {
-          const float mn = need ? tmu : m;
-          const float corr = fast_exp2(m - mn);
-          l *= corr;
+          for (int r = 0; r < 16; ++r) t = fmaxf(t, sa[ks][r]);
+        t = fmaxf(t, xor_shfl(t, 32));
+        update_max(t, c2, m, corr, any);
+      }
+      for (;;) {
+        // step A: current = (kb, 0) in sa, next = (kb, 1) -> sb
+        vm_wait();
+        __syncthreads();
+        if (kbn >= 0) issue_k(kbn, 0, LK0);
+        issue_v(kb, 1, LV1);
+        l *= corr;
+        qk_softmax<D, true>(kbuf1, koff, qf, sb, sa, c2, -m, pb, l);
+        if (any) {
 #pragma unroll
           for (int ds = 0; ds < D / 32; ++ds)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[ds][r] *= corr;
-          m = mn;
         }
-        const float nm = -m;
-        bf16x8 pb[4];
-        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            uint32_t wv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float a0 = fast_exp2(fmaf(s[ks][8 * c + 2 * e], c2, nm));
-              const float a1 = fast_exp2(fmaf(s[ks][8 * c + 2 * e + 1], c2, nm));
-              wv[e] = pack_bf16x2(a0, a1);
-              // the row sum uses the rounded weights, the same ones the PV product uses
-              l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv[e]), one2, l, false);
-            }
-            pb[2 * ks + c] = as_bf16x8(make_uint4(wv[0], wv[1], wv[2], wv[3]));
-          }
+        if (kb == qb) mask_diag(sb, KS, qloc, lane);
+        update_max(pv_max<D, true>(vbuf0, voff, pb, o, sb), c2, m, corr, any);
+
+        // step B: current = (kb, 1) in sb, next = (kbn, 0) -> sa
+        vm_wait();
+        __syncthreads();
+        l *= corr;
+        if (kbn >= 0) {
+          issue_k(kbn, 1, LK1);
+          issue_v(kbn, 0, LV0);
         }
-        const char* vr = vbuf + vrow * S::VROW;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
+        // one straight-line path whether or not a next block exists (the
+        // scores and maximum computed from the stale buffer at a row's end are
+        // not used), so that the accumulators stay in place across the loop
+        qk_softmax<D, true>(kbuf0, koff, qf, sa, sb, c2, -m, pb, l);
+        if (any) {
 #pragma unroll
           for (int ds = 0; ds < D / 32; ++ds)
-            o[ds] = mfma_32x32x16(as_bf16x8(ld16(vr + 32 * ds * S::VROW + ((2 * cc + hi) ^ vfix) * 16)), pb[cc], o[ds]);
-      }
-      if (hf == 0) {
-        hf = 1;
-      } else {
-        hf = 0;
-        t = tn;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[ds][r] *= corr;
+        }
+        if (kbn == qb) mask_diag(sa, 0, qloc, lane);
+        const float tn = pv_max<D, true>(vbuf1, voff, pb, o, sa);
+        if (kbn < 0) break;
+        update_max(tn, c2, m, corr, any);
         kb = kbn;
-        tn = t + 1;
-        kbn = tn < t1 ? kb_at(tn) : -1;
+        pc = pn;
+        pn = next_valid(pc + 1);
+        kbn = pn < t1 ? entry(pn) : -1;
       }
-      bf ^= 1;
     }
 
     l += xor_shfl(l, 32);
