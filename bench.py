@@ -47,6 +47,9 @@ def parse():
                     help="measured HBM bytes per attention launch (JSON), if current")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a device copy of this many MiB (HBM counter calibration) and exit")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only sweep the sequence length (Llama-shaped layers, 4k-128k) and report where the "
+                         "sparse path overtakes dense attention")
     return ap.parse_args()
 
 
@@ -66,7 +69,7 @@ class Layer:
         from prefill_inputs import WORKLOADS, workload_inputs
 
         self.crisp = crisp
-        self.wl = WORKLOADS[idx]
+        self.wl = WORKLOADS[idx] if isinstance(idx, int) else idx
         sh = self.wl.shape
         t0 = time.perf_counter()
         self.inp = workload_inputs(self.wl)
@@ -215,6 +218,32 @@ def cpu_baseline(layer, res, rp, col):
             "stage_ms": {"route_select": round(t_sel_layer * 1e3, 1), "attn": round(t_attn_layer * 1e3, 1)}}
 
 
+def crossover_workload(n):
+    """A Llama-shaped layer of n tokens from the 128k layer's recipe (75% VS heads,
+    sink scale 3), with the planted vertical keys scaled with n."""
+    from prefill_inputs import Shape, Workload
+    return Workload(name=f"llama3_8b_layer_n{n}", shape=Shape(1, n, 32, 8, 128), vs_fraction=0.75,
+                    sink_scale=3.0, n_vert=max(4, round(64 * n / 131072)), alphas=(1.0,),
+                    seed=9000 + n.bit_length())
+
+
+def crossover(args):
+    """Sparse layer (route + select + attention) vs dense attention over n."""
+    rows = []
+    for n in (4096, 8192, 10240, 12288, 14336, 16384, 32768, 65536, 131072):
+        layer = Layer(crossover_workload(n))
+        res = layer.measure(1.0, max(args.steps, 5), max(args.warmup, 2))
+        dense_ms, _ = layer.dense(max(args.dense_steps, 5))
+        rows.append(dict(n=n, sparse_ms=round(res["ms_per_layer"], 3), stage_ms=res["stage_ms"],
+                         dense_ms=round(dense_ms, 3), tile_fraction=round(res["tile_fraction"], 4),
+                         speedup=round(dense_ms / res["ms_per_layer"], 3)))
+        log(f"[crossover] n={n}: sparse {res['ms_per_layer']:.3f} ms (route {res['stage_ms']['route']:.3f}, "
+            f"select {res['stage_ms']['select']:.3f}), dense {dense_ms:.3f} ms, x{dense_ms / res['ms_per_layer']:.2f}")
+        layer.free()
+    first = next((r["n"] for r in rows if r["speedup"] > 1.0), None)
+    print(json.dumps({"crossover": rows, "sparse_faster_from_n": first}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -233,6 +262,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_kernel": "torch.add(uint8, 1)", "read_bytes_per_launch": nbytes,
                           "write_bytes_per_launch": nbytes, "launches": 3}))
+        return
+
+    if args.crossover:
+        crossover(args)
         return
 
     idx = ALIASES.get(args.workload) or int(args.workload)

@@ -159,10 +159,26 @@ int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg,
 /* Dense exact causal attention (the result FlashAttention computes; digest,
  * prerequisite section on FlashAttention): crisp_sparse_attn with every key
  * block kb <= qb selected, same kernels and precision.
- * ws: crisp_workspace_bytes(CRISP_CALL_DENSE) bytes (a few counters). */
+ * ws: crisp_workspace_bytes(CRISP_CALL_DENSE) bytes (work-queue counters and
+ * a V^T copy of V, as for crisp_sparse_attn). */
 int dense_attn(const crisp_shape* shape, const void* q_bf16, const void* k_bf16,
                const void* v_bf16, void* out, int out_dtype, void* ws, size_t ws_bytes,
                void* stream);
+
+/* Sequence length below which the sparse path does not pay for itself.
+ * Routing and selection cost a fixed ~0.4 ms and a short causal map has few
+ * tiles to skip, so dense attention wins on short inputs (the digest's
+ * limitations paragraph, item 7, reports the same, with the crossover between
+ * 8K and 64K tokens on its GPU).  Measured on one MI355X with Llama-shaped
+ * layers (32 query / 8 KV heads, d = 128, 75% VS heads): dense / sparse layer
+ * time 0.87 at n = 8192 and 1.12 at n = 10240. */
+#define CRISP_DENSE_BELOW_TOKENS 10240
+
+/* Which path a prefill of this shape takes: *use_dense = 1 when
+ * shape->n < CRISP_DENSE_BELOW_TOKENS (call dense_attn), else 0 (call
+ * crisp_route, crisp_select and crisp_sparse_attn).  The shape is validated
+ * as for the other calls.  Pure host logic; returns a status. */
+int crisp_use_dense(const crisp_shape* shape, int32_t* use_dense);
 
 /* Static description of a status code. */
 const char* crisp_status_string(int status);

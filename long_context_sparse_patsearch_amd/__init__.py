@@ -19,7 +19,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["CrispError", "config", "shape_of", "workspace_bytes", "max_blocks", "route", "select",
+__all__ = ["CrispError", "config", "shape_of", "workspace_bytes", "max_blocks", "use_dense", "route", "select",
            "sparse_attn", "dense_attn", "prefill", "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +64,7 @@ def load():
     ps, pc = ctypes.POINTER(Shape), ctypes.POINTER(Cfg)
     lib.crisp_workspace_bytes.argtypes = [ps, pc, I, ctypes.POINTER(SZ)]
     lib.crisp_max_blocks.argtypes = [ps, ctypes.POINTER(I64)]
+    lib.crisp_use_dense.argtypes = [ps, ctypes.POINTER(ctypes.c_int32)]
     lib.crisp_route.argtypes = [ps, pc, P, P, P, P, P, P, P, SZ, P]
     lib.crisp_select.argtypes = [ps, pc, P, P, P, P, P, P, P, I64, P, P, SZ, P]
     lib.crisp_sparse_attn.argtypes = [ps, pc, P, P, P, P, P, I64, P, I, P, SZ, P]
@@ -71,7 +72,7 @@ def load():
     lib.crisp_status_string.argtypes = [I]
     lib.crisp_status_string.restype = ctypes.c_char_p
     lib.crisp_last_error.restype = ctypes.c_char_p
-    for f in ("crisp_workspace_bytes", "crisp_max_blocks", "crisp_route", "crisp_select",
+    for f in ("crisp_workspace_bytes", "crisp_max_blocks", "crisp_use_dense", "crisp_route", "crisp_select",
               "crisp_sparse_attn", "dense_attn"):
         getattr(lib, f).restype = I
     _lib = lib
@@ -131,6 +132,13 @@ def max_blocks(shape: Shape) -> int:
     out = ctypes.c_int64(0)
     _check(load().crisp_max_blocks(ctypes.byref(shape), ctypes.byref(out)))
     return out.value
+
+
+def use_dense(shape: Shape) -> bool:
+    """True when a prefill of this shape should run dense attention (short inputs)."""
+    out = ctypes.c_int32(0)
+    _check(load().crisp_use_dense(ctypes.byref(shape), ctypes.byref(out)))
+    return bool(out.value)
 
 
 def _workspace(nbytes, device, ws=None):
@@ -219,10 +227,17 @@ def dense_attn(q, k, v, out=None, out_dtype=None, ws=None, stream=None):
     return out
 
 
-def prefill(q, k, v, cfg: Cfg | None = None, out_dtype=None, stream=None) -> dict:
-    """The whole method on one layer: route, select, sparse attention."""
+def prefill(q, k, v, cfg: Cfg | None = None, out_dtype=None, stream=None, gate: bool = True) -> dict:
+    """The whole method on one layer: route, select, sparse attention.
+
+    With gate=True, inputs shorter than the library's crossover length
+    (crisp_use_dense) run dense attention instead; 'path' says which ran."""
     cfg = cfg or config()
+    _check_qkv(q, k, v)
+    if gate and use_dense(shape_of(q, k)):
+        return dict(route=None, select=None, out=dense_attn(q, k, v, out_dtype=out_dtype, stream=stream),
+                    path="dense")
     r = route(q, k, cfg, stream=stream)
     s = select(q, k, r, cfg, stream=stream)
     o = sparse_attn(q, k, v, s, cfg, out_dtype=out_dtype, stream=stream)
-    return dict(route=r, select=s, out=o)
+    return dict(route=r, select=s, out=o, path="sparse")

@@ -119,6 +119,15 @@ int crisp_max_blocks(const crisp_shape* shape, int64_t* blocks) {
   return CRISP_OK;
 }
 
+int crisp_use_dense(const crisp_shape* shape, int32_t* use_dense) {
+  Dims dm;
+  const int st = make_dims(shape, &dm);
+  if (st) return st;
+  if (!use_dense) return CRISP_ERR_NULL;
+  *use_dense = dm.n < CRISP_DENSE_BELOW_TOKENS ? 1 : 0;
+  return CRISP_OK;
+}
+
 int crisp_route(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
                 float* c_struct, int8_t* pattern, float* p_vert, float* p_slash, void* ws, size_t ws_bytes,
                 void* stream) {

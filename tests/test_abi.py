@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_method_calls():
     names = declared_functions()
-    for f in ("crisp_route", "crisp_select", "crisp_sparse_attn", "dense_attn",
+    for f in ("crisp_route", "crisp_select", "crisp_sparse_attn", "dense_attn", "crisp_use_dense",
               "crisp_workspace_bytes", "crisp_max_blocks", "crisp_status_string", "crisp_last_error"):
         assert f in names
 
@@ -81,6 +81,18 @@ def test_workspace_and_capacity_queries(lib):
     assert lib.crisp_workspace_bytes(ctypes.byref(sh), ctypes.byref(cfg), 9, ctypes.byref(n)) == PARAM
     assert lib.crisp_workspace_bytes(ctypes.byref(sh), ctypes.byref(cfg), 0, None) == NULL
     assert crisp.workspace_bytes(shape(batch=0), cfg, 1) == 0
+
+
+def test_dense_gate(lib):
+    """Short inputs take the dense path: the threshold is the header's CRISP_DENSE_BELOW_TOKENS."""
+    limit = int(re.search(r"#define\s+CRISP_DENSE_BELOW_TOKENS\s+(\d+)", open(HEADER).read()).group(1))
+    assert limit % 128 == 0 and 8192 < limit <= 65536
+    for n, want in ((384, True), (4096, True), (limit - 128, True), (limit, False), (131072, False)):
+        assert crisp.use_dense(shape(n=n)) is want, n
+    flag = ctypes.c_int32(7)
+    assert lib.crisp_use_dense(ctypes.byref(shape(n=4096 + 64)), ctypes.byref(flag)) == SHAPE
+    assert lib.crisp_use_dense(ctypes.byref(shape()), None) == NULL
+    assert lib.crisp_use_dense(None, ctypes.byref(flag)) == NULL
 
 
 def _route(lib, sh, cfg, ptrs, ws_bytes):

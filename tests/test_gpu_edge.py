@@ -179,3 +179,26 @@ def test_empty_batch_is_a_no_op():
     d = crisp.dense_attn(q, k, k)
     torch.cuda.synchronize()
     assert r["pattern"].numel() == 0 and o.numel() == 0 and d.numel() == 0 and s["row_ptr"].numel() == 1
+
+
+@pytest.mark.parametrize("n", [4096, 10240])
+def test_prefill_length_gate(n):
+    """prefill() runs dense attention below the library's crossover length and
+    the sparse path from it on; either way the output is exactly what the
+    chosen path's own calls give (those are checked against the oracle above)."""
+    sh = Shape(1, n, 4, 2, 64)
+    q, k, v = device_inputs(_inputs(sh, seed=61))
+    cfg = crisp.config()
+    res = crisp.prefill(q, k, v, cfg)
+    want_dense = n < 10240
+    assert crisp.use_dense(crisp.shape_of(q, k)) is want_dense
+    assert res["path"] == ("dense" if want_dense else "sparse")
+    if want_dense:
+        ref = crisp.dense_attn(q, k, v)
+    else:
+        r = crisp.route(q, k, cfg)
+        ref = crisp.sparse_attn(q, k, v, crisp.select(q, k, r, cfg), cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(res["out"], ref)
+    ungated = crisp.prefill(q, k, v, cfg, gate=False)
+    assert ungated["path"] == "sparse" and ungated["route"] is not None
