@@ -46,6 +46,17 @@ R14 Grouped KV heads: query head h uses KV head floor(h / (h_q / h_kv)); routing
     and selection are per query head.
 R15 If the whole flattened PE map sums to less than gamma (rounding), every
     entry is kept.
+R18 FlexPrefill's JSD router (the method CRISP replaces): a_hat is the proxy's
+    "softmax, then average" key-block distribution, i.e. p_v of R4; a_bar is
+    the "pool, then softmax" estimate: the b proxy queries mean-pooled into one
+    query against the mean-pooled key of every block, logits / sqrt(d), softmax
+    over all N_b blocks (the last query block sees every key block).  D_JS uses
+    the natural log; the head routes VS iff D_JS >= tau_jsd.  The pages give
+    no value for tau_jsd; it is a parameter.
+R19 FlexPrefill's VS index is Algorithm 3 with the per-direction noise-floor
+    rule replaced by the gamma-cumsum budget rule (same gamma as the PE path):
+    the shortest descending prefix of p_d reaching gamma, its count clipped to
+    [k_min, N_b] (top-k), then the anchors {0, N_b-1}.
 """
 from __future__ import annotations
 
@@ -295,6 +306,87 @@ def crisp_head(q_h, k_g, *, tau=0.2, alpha=1.0, gamma=0.95, k_min_tokens=1024,
         ss, mu_s, cnt_s = noise_floor_select(p_s, alpha, kmin)
         res.update(sel_v=sv, sel_s=ss, mu_v=mu_v, mu_s=mu_s, cnt_v=cnt_v, cnt_s=cnt_s,
                    rows=vs_rows(sv, ss, nb))
+    else:
+        pe = pe_select(pooled_map(q_h, k_g, block), gamma)
+        res.update(pe=pe, rows=pe["rows"])
+    return res
+
+
+# ----------------------------------------------------------------------------
+# the FlexPrefill baseline path (the routing and VS budget rule CRISP replaces)
+# ----------------------------------------------------------------------------
+def pooled_proxy_estimate(q_h: np.ndarray, k_g: np.ndarray, b: int = BLOCK, block: int = BLOCK) -> np.ndarray:
+    """a_bar: the "pool first, then softmax" estimate of the proxy's key-block distribution (R18).
+
+    [digest] prerequisite section on Jensen-Shannon divergence.  Returns N_b
+    probabilities summing to 1.
+    """
+    n, d = q_h.shape
+    nb = n // block
+    qbar = q_h[n - b:].mean(axis=0)
+    kbar = k_g.reshape(nb, block, d).mean(axis=1)
+    s = (kbar @ qbar) / math.sqrt(d)
+    e = np.exp(s - s.max())
+    return e / e.sum()
+
+
+def jensen_shannon(p: np.ndarray, q: np.ndarray) -> float:
+    """D_JS = 1/2 KL(p || m) + 1/2 KL(q || m) with m = (p + q) / 2, natural log.
+
+    [digest] prerequisite section on Jensen-Shannon divergence.  Terms with a
+    zero numerator contribute 0.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    m = 0.5 * (p + q)
+    def kl(a):
+        nz = a > 0
+        return float(np.sum(a[nz] * np.log(a[nz] / m[nz])))
+    return 0.5 * kl(p) + 0.5 * kl(q)
+
+
+def jsd_route(d_js: float, tau_jsd: float) -> bool:
+    """FlexPrefill's router: Vertical-Slash iff D_JS >= tau_jsd (R18, R8)."""
+    return bool(d_js >= tau_jsd)
+
+
+def gamma_direction_select(p: np.ndarray, gamma: float, k_min_blocks: int):
+    """FlexPrefill's budget rule for one VS direction (R19).
+
+    The gamma-cumsum set of p (ties to the lower index), its count clipped to
+    [k_min, N_b] by taking the top-k, then the anchors 0 and N_b-1.  [digest]
+    prerequisite section on the cumulative-coverage threshold and the Algorithm
+    3 caption.  Returns (sorted selected blocks, size of the gamma-cumsum set).
+    """
+    nb = len(p)
+    kept, order, _ = gamma_cumsum(np.asarray(p, dtype=np.float64), gamma)
+    k = min(max(len(kept), k_min_blocks), nb)
+    sel = {0, nb - 1}.union(order[:k].tolist())
+    return np.array(sorted(sel), dtype=np.int64), len(kept)
+
+
+def flex_head(q_h, k_g, *, tau_jsd=0.1, gamma=0.95, k_min_tokens=1024, block=BLOCK, force_vs=None):
+    """FlexPrefill's routing and selection of one query head, the baseline the pages compare with.
+
+    The same proxy as PatSearch; JSD routing between a_hat = p_v and the pooled
+    estimate a_bar (R18); VS heads take the gamma-cumsum budget rule in both
+    directions (R19), PE heads the same PEIndex as CRISP.  ``force_vs``
+    overrides the routing decision.
+    """
+    n = q_h.shape[0]
+    nb = n // block
+    a_hat = proxy_attention(q_h, k_g, block)
+    p_v, p_s = vs_scores(a_hat, block)
+    del a_hat
+    a_bar = pooled_proxy_estimate(q_h, k_g, block, block)
+    d_js = jensen_shannon(p_v, a_bar)
+    is_vs = jsd_route(d_js, tau_jsd) if force_vs is None else bool(force_vs)
+    res = dict(jsd=d_js, is_vs=is_vs, p_v=p_v, p_s=p_s, a_bar=a_bar)
+    if is_vs:
+        kmin = k_min_tokens // block
+        sv, cnt_v = gamma_direction_select(p_v, gamma, kmin)
+        ss, cnt_s = gamma_direction_select(p_s, gamma, kmin)
+        res.update(sel_v=sv, sel_s=ss, cnt_v=cnt_v, cnt_s=cnt_s, rows=vs_rows(sv, ss, nb))
     else:
         pe = pe_select(pooled_map(q_h, k_g, block), gamma)
         res.update(pe=pe, rows=pe["rows"])

@@ -325,3 +325,85 @@ def check_alpha_zero_is_dense(co, seed=9):
     o_d = co.dense_attention(q, k, v)
     for qb in range(nb):
         assert np.array_equal(o_s[qb], o_d[qb])
+
+
+# --- the FlexPrefill baseline path --------------------------------------------
+def check_jsd_against_library(co, seed=20):
+    """D_JS against scipy's Jensen-Shannon distance (natural log; scipy returns
+    the square root), plus its fixed values: 0 for equal arguments, ln 2 for
+    disjoint supports, symmetry."""
+    from scipy.spatial.distance import jensenshannon
+    rng = np.random.default_rng(seed)
+    for n in (2, 7, 64):
+        p, q = rng.random(n), rng.random(n)
+        p[rng.random(n) < 0.3] = 0.0
+        p, q = p / p.sum(), q / q.sum()
+        want = float(jensenshannon(p, q)) ** 2
+        assert math.isclose(co.jensen_shannon(p, q), want, rel_tol=1e-10, abs_tol=1e-14)
+        assert math.isclose(co.jensen_shannon(p, q), co.jensen_shannon(q, p), rel_tol=1e-12)
+        assert abs(co.jensen_shannon(p, p)) < 1e-15
+    assert math.isclose(co.jensen_shannon(np.array([1.0, 0, 0]), np.array([0, 0.5, 0.5])), math.log(2), rel_tol=1e-12)
+
+
+def check_pooled_estimate_brute_force(co, seed=21):
+    """a_bar: mean of the last b queries against each block's mean key, scaled
+    softmax over every block, written out with loops."""
+    rng = np.random.default_rng(seed)
+    nb, d = 5, 16
+    n = nb * B
+    q, k = _rand(rng, n, d), _rand(rng, n, d)
+    got = co.pooled_proxy_estimate(q, k, B, B)
+    qm = [sum(q[n - B + i, c] for i in range(B)) / B for c in range(d)]
+    logits = []
+    for blk in range(nb):
+        km = [sum(k[blk * B + j, c] for j in range(B)) / B for c in range(d)]
+        logits.append(sum(qm[c] * km[c] for c in range(d)) / math.sqrt(d))
+    w = np.exp(np.array(logits) - max(logits))
+    assert np.allclose(got, w / w.sum(), rtol=1e-12)
+
+
+def check_gamma_direction_brute_force(co, seed=22):
+    """The gamma-cumsum set of one direction is a smallest subset reaching gamma
+    (brute force over every subset of 8 blocks), ties go to the lower index,
+    the count is clipped to [k_min, N_b] and the anchors are added."""
+    import itertools
+    rng = np.random.default_rng(seed)
+    nb = 8
+    for trial in range(20):
+        p = rng.random(nb) ** 3
+        if trial % 4 == 0:
+            p[2] = p[5]                      # a tie
+        p /= p.sum()
+        for gamma in (0.3, 0.7, 0.95, 1.0 - 1e-12):
+            best = min(len(c) for r in range(1, nb + 1) for c in itertools.combinations(range(nb), r)
+                       if sum(p[list(c)]) >= gamma)
+            sel, cnt = co.gamma_direction_select(p, gamma, 0)
+            assert cnt == best
+            core = sorted(np.lexsort((np.arange(nb), -p))[:best].tolist())
+            assert sorted(set(core) | {0, nb - 1}) == sel.tolist()
+            for kmin in (3, 6, 20):
+                sel_k, _ = co.gamma_direction_select(p, gamma, kmin)
+                k = min(max(best, kmin), nb)
+                top = np.lexsort((np.arange(nb), -p))[:k].tolist()
+                assert sel_k.tolist() == sorted(set(top) | {0, nb - 1})
+    # tie toward the lower index: two equal largest scores, gamma reached by one of them
+    p = np.array([0.1, 0.4, 0.1, 0.4, 0.0, 0.0, 0.0, 0.0])
+    sel, cnt = co.gamma_direction_select(p, 0.35, 0)
+    assert cnt == 1 and sel.tolist() == [0, 1, 7]
+
+
+def check_flex_routes_planted(co):
+    """The JSD router sends the planted VS head of the 4k workload to VS and the
+    diffuse head to PE (the pages: JSD reproduces C_struct's decisions on such
+    heads), and its VS sets keep the sink block and the planted vertical blocks."""
+    from prefill_inputs import WORKLOADS, workload_inputs
+    inp = workload_inputs(WORKLOADS[1])
+    q0, k0 = co.bf16_to_f64(inp["q"][0, 0]), co.bf16_to_f64(inp["k"][0, 0])
+    q1, k1 = co.bf16_to_f64(inp["q"][0, 1]), co.bf16_to_f64(inp["k"][0, 1])
+    r0 = co.flex_head(q0, k0, tau_jsd=0.1)
+    r1 = co.flex_head(q1, k1, tau_jsd=0.1)
+    assert r0["is_vs"] and r0["jsd"] > 0.2
+    assert not r1["is_vs"] and r1["jsd"] < 0.02
+    planted = set((np.asarray(inp["planted"][0][0]["vert"]) // B).tolist())
+    assert len(planted) > 0
+    assert 0 in r0["sel_v"].tolist() and planted <= set(r0["sel_v"].tolist())

@@ -34,6 +34,14 @@ MUTANTS = {
     "attn_no_scale": ("    scale = 1.0 / math.sqrt(d)\n    out = {}", "    scale = 1.0\n    out = {}"),
     "attn_not_causal": ("        vis = keys[None, :] <= qpos[:, None]", "        vis = keys[None, :] >= 0"),
     "attn_v_misindexed": ("        out[qb] = (e @ v_g[keys]) / den", "        out[qb] = (e @ v_g[np.sort(keys)[::-1]]) / den"),
+    "jsd_log2": ("        return float(np.sum(a[nz] * np.log(a[nz] / m[nz])))",
+                 "        return float(np.sum(a[nz] * np.log2(a[nz] / m[nz])))"),
+    "jsd_m_not_halved": ("    m = 0.5 * (p + q)\n", "    m = p + q\n"),
+    "jsd_route_flipped": ("    return bool(d_js >= tau_jsd)", "    return bool(d_js < tau_jsd)"),
+    "pooled_est_all_queries": ("    qbar = q_h[n - b:].mean(axis=0)", "    qbar = q_h.mean(axis=0)"),
+    "pooled_est_no_scale": ("    s = (kbar @ qbar) / math.sqrt(d)", "    s = (kbar @ qbar)"),
+    "flex_no_kmin": ("    k = min(max(len(kept), k_min_blocks), nb)", "    k = min(len(kept), nb)"),
+    "flex_no_anchors": ("    sel = {0, nb - 1}.union(order[:k].tolist())", "    sel = set(order[:k].tolist())"),
     "bf16_decode_shift": ("    w = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)",
                           "    w = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)"),
 }
