@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flex", action="store_true", help="skip the FlexPrefill baseline path")
+    ap.add_argument("--tau-jsd", type=float, default=0.1, help="JSD threshold of the FlexPrefill router")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per attention launch (JSON), if current")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -138,6 +140,50 @@ class Layer:
                     pe_heads=int(len(pattern) - pattern.sum()), attn_flop=flop,
                     attn_tflops=flop / (st["attn"] * 1e-3) / 1e12, _pattern=pattern)
 
+    def flex_step(self, cfg, tau_jsd, evs=None):
+        c = self.crisp
+        if evs:
+            evs[0].record()
+        c.route(self.q, self.k, cfg, out=self.r_out, ws=self.ws_r)
+        if evs:
+            evs[1].record()
+        f = c.flex_route(self.q, self.k, self.r_out, tau_jsd, cfg, out=self.f_out, ws=self.ws_f)
+        if evs:
+            evs[2].record()
+        c.flex_select(self.q, self.k, f, cfg, out=self.s_out, ws=self.ws_s)
+        if evs:
+            evs[3].record()
+        c.sparse_attn(self.q, self.k, self.v, self.s_out, cfg, out=self.o)
+        if evs:
+            evs[4].record()
+
+    def measure_flex(self, alpha, tau_jsd, steps, warmup):
+        """The FlexPrefill baseline path on the same layer (JSD routing, gamma-cumsum VS budget)."""
+        import torch
+        cfg = self.cfg(alpha)
+        dev = self.q.device
+        self.f_out = dict(jsd=torch.empty(self.bh, dtype=torch.float32, device=dev),
+                          pattern=torch.empty(self.bh, dtype=torch.int8, device=dev))
+        self.ws_f = torch.empty(max(1, self.crisp.workspace_bytes(self.shape, cfg, self.crisp.CALL_FLEX_ROUTE)),
+                                dtype=torch.uint8, device=dev)
+        for _ in range(warmup):
+            self.flex_step(cfg, tau_jsd)
+        torch.cuda.synchronize()
+        evs = [[_event() for _ in range(5)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.flex_step(cfg, tau_jsd, evs[i])
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        names = ("route", "flex_route", "select", "attn")
+        st = {nm: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, nm in enumerate(names)}
+        tiles = int(self.s_out["row_ptr"][-1].item())
+        pattern = self.f_out["pattern"].cpu().numpy()
+        self.f_out = self.ws_f = None
+        return dict(workload=self.wl.name, tau_jsd=tau_jsd, gamma=self.wl.gamma, ms_per_layer=round(wall_ms, 3),
+                    stage_ms={k_: round(v_, 4) for k_, v_ in st.items()}, tiles=tiles,
+                    vs_heads=int(pattern.sum()), pe_heads=int(len(pattern) - pattern.sum()))
+
     def dense(self, steps):
         import torch
         c = self.crisp
@@ -160,7 +206,7 @@ class Layer:
 
     def free(self):
         import torch
-        for name in ("q", "k", "v", "o", "ws_r", "ws_s", "s_out", "r_out"):
+        for name in ("q", "k", "v", "o", "ws_r", "ws_s", "s_out", "r_out", "f_out", "ws_f"):
             setattr(self, name, None)
         torch.cuda.empty_cache()
 
@@ -216,6 +262,27 @@ def cpu_baseline(layer, res, rp, col):
                        f"{res['tiles']} selected tiles) of {wl.name}, extrapolated linearly to one layer; "
                        f"measured {t_sel:.1f}s + {t_attn:.1f}s"),
             "stage_ms": {"route_select": round(t_sel_layer * 1e3, 1), "attn": round(t_attn_layer * 1e3, 1)}}
+
+
+def stage_rates(sh, res):
+    """Algorithmic bytes / time of the routing and selection stages (GB/s).
+
+    route: the two proxy passes each read every KV head's K once, plus the 128
+    proxy query rows of every head.  select: PEIndex reads the Q of its PE
+    heads and the K of every KV group holding one, then passes over each PE
+    head's triangular map of N_b(N_b+1)/2 fp32 scores six times (logits
+    written; softmax read and written; three radix passes read)."""
+    kv = sh.batch * sh.h_kv * sh.n * sh.d * 2
+    route_b = 2 * kv + sh.batch * sh.h_q * 128 * sh.d * 2
+    pe = res["pe_heads"]
+    g = sh.h_q // sh.h_kv
+    pe_groups = min(sh.batch * sh.h_kv, pe)   # at most one group per PE head
+    tri = sh.n_blocks * (sh.n_blocks + 1) // 2
+    sel_b = pe * sh.n * sh.d * 2 + pe_groups * sh.n * sh.d * 2 + 6 * 4 * tri * pe
+    del g
+    return {"route": round(route_b / (res["stage_ms"]["route"] * 1e-3) / 1e9, 1), "route_bytes": route_b,
+            "select": round(sel_b / (res["stage_ms"]["select"] * 1e-3) / 1e9, 1), "select_bytes": sel_b,
+            "peak_hbm_gbs": 8000.0}
 
 
 def crossover_workload(n):
@@ -277,7 +344,7 @@ def main():
     for j, _ in specs:
         if j not in order:
             order.append(j)
-    results, dense, keep = [], {}, None
+    results, dense, keep, flex = [], {}, None, []
     for j in order:
         layer = Layer(j)
         for jj, a in specs:
@@ -294,6 +361,18 @@ def main():
             if r["_primary"]:
                 rp, col = layer.host_csr()
                 keep = (layer, rp, col, r)
+        if not args.no_flex:
+            a0 = next(a for jj, a in specs if jj == j)
+            a0 = layer.wl.alphas[0] if a0 is None else a0
+            fr = layer.measure_flex(a0, args.tau_jsd, args.steps, args.warmup)
+            crisp_r = next(r for r in results if r["workload"] == layer.wl.name and r["alpha"] == a0)
+            fr["crisp_ms"] = round(crisp_r["ms_per_layer"], 3)
+            fr["crisp_tiles"] = crisp_r["tiles"]
+            fr["crisp_speedup_over_flex"] = round(fr["ms_per_layer"] / crisp_r["ms_per_layer"], 3)
+            flex.append(fr)
+            log(f"[bench] {layer.wl.name} FlexPrefill (tau_jsd={args.tau_jsd}, gamma={layer.wl.gamma}): "
+                f"{fr['ms_per_layer']:.2f} ms/layer {fr['stage_ms']} tiles={fr['tiles']}; CRISP is "
+                f"x{fr['crisp_speedup_over_flex']:.3f} faster")
         if not args.no_dense:
             dense[layer.wl.name] = layer.dense(args.dense_steps)
             log(f"[bench] {layer.wl.name} dense: {dense[layer.wl.name][0]:.1f} ms "
@@ -346,6 +425,15 @@ def main():
         "also": [{k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in x.items() if not k_.startswith("_")}
                  for x in also],
     }
+    # effective rate over the unmasked causal (query, key) pairs of the selected tiles (every row keeps
+    # its diagonal tile, of which 128*129/2 pairs are unmasked), and the routing / selection byte rates
+    sh = layer.wl.shape
+    rows = sh.batch * sh.h_q * sh.n_blocks
+    pairs = res["tiles"] * 128 * 128 - rows * (128 * 128 - 128 * 129 // 2)
+    out["attn_tflops_causal_pairs"] = round(4 * sh.d * pairs / (res["stage_ms"]["attn"] * 1e-3) / 1e12, 2)
+    out["selection_gbs"] = stage_rates(sh, res)
+    if flex:
+        out["flexprefill"] = flex
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(layer, res, rp, col)

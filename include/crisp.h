@@ -82,7 +82,10 @@ enum crisp_status {
 
 enum crisp_out_dtype { CRISP_OUT_F32 = 0, CRISP_OUT_BF16 = 1 };
 
-enum crisp_call { CRISP_CALL_ROUTE = 0, CRISP_CALL_SELECT = 1, CRISP_CALL_ATTN = 2, CRISP_CALL_DENSE = 3 };
+enum crisp_call {
+  CRISP_CALL_ROUTE = 0, CRISP_CALL_SELECT = 1, CRISP_CALL_ATTN = 2, CRISP_CALL_DENSE = 3,
+  CRISP_CALL_FLEX_ROUTE = 4, CRISP_CALL_FLEX_SELECT = 5
+};
 
 /* Device workspace in bytes that `call` needs for this shape (pure host
  * arithmetic, no HIP call).  Writes *bytes; returns a status.  The workspace
@@ -164,6 +167,35 @@ int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg,
 int dense_attn(const crisp_shape* shape, const void* q_bf16, const void* k_bf16,
                const void* v_bf16, void* out, int out_dtype, void* ws, size_t ws_bytes,
                void* stream);
+
+/* The FlexPrefill baseline: the routing and VS budget rule that CRISP
+ * replaces, on the same kernels (digest: prerequisite sections on
+ * Jensen-Shannon divergence and on the cumulative-coverage threshold).
+ *
+ * flex_route: given p_vert from crisp_route (a_hat, the proxy's block-pooled
+ * key distribution), forms a_bar[kb] = softmax over key blocks of
+ * mean(last 128 query rows) . mean(K rows of block kb) / sqrt(d), and writes
+ * jsd[bh] = D_JS(a_hat, a_bar) = 1/2 KL(a_hat||m) + 1/2 KL(a_bar||m),
+ * m = (a_hat + a_bar)/2, natural log, and pattern[bh] = 1 (VS) iff
+ * jsd >= tau_jsd, else 0 (PE).  The pages give no value for tau_jsd.
+ * q, k as for crisp_route; p_vert [batch*h_q][N_b] fp32 (device, read);
+ * jsd [batch*h_q] fp32 and pattern [batch*h_q] int8 (device, written).
+ * ws: crisp_workspace_bytes(CRISP_CALL_FLEX_ROUTE) bytes (pooled keys).
+ * Errors: as crisp_route; CRISP_ERR_PARAM for a negative or non-finite tau_jsd. */
+int flex_route(const crisp_shape* shape, const crisp_cfg* cfg, float tau_jsd, const void* q_bf16,
+               const void* k_bf16, const float* p_vert, float* jsd, int8_t* pattern, void* ws,
+               size_t ws_bytes, void* stream);
+
+/* flex_select: crisp_select with the per-direction VS rule replaced by the
+ * gamma-cumsum budget (cfg->gamma): the shortest prefix of p_d sorted
+ * descending (ties to the lower block) whose sum reaches gamma, its count
+ * clipped to [k_min, N_b], then the anchor blocks 0 and N_b-1.  PE heads,
+ * the CSR and every argument and error are as for crisp_select (cfg->alpha
+ * is not used).  ws: crisp_workspace_bytes(CRISP_CALL_FLEX_SELECT) bytes. */
+int flex_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
+                const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
+                int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws, size_t ws_bytes,
+                void* stream);
 
 /* Sequence length below which the sparse path does not pay for itself.
  * Routing and selection cost a fixed ~0.4 ms and a short causal map has few

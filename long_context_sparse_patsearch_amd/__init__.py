@@ -20,13 +20,14 @@ import ctypes
 import os
 
 __all__ = ["CrispError", "config", "shape_of", "workspace_bytes", "max_blocks", "use_dense", "route", "select",
-           "sparse_attn", "dense_attn", "prefill", "library_path", "load"]
+           "sparse_attn", "dense_attn", "prefill", "flex_route", "flex_select", "flex_prefill", "library_path",
+           "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcrisp.so")
 _lib = None
 
-CALL_ROUTE, CALL_SELECT, CALL_ATTN, CALL_DENSE = 0, 1, 2, 3
+CALL_ROUTE, CALL_SELECT, CALL_ATTN, CALL_DENSE, CALL_FLEX_ROUTE, CALL_FLEX_SELECT = 0, 1, 2, 3, 4, 5
 OUT_F32, OUT_BF16 = 0, 1
 
 
@@ -69,11 +70,13 @@ def load():
     lib.crisp_select.argtypes = [ps, pc, P, P, P, P, P, P, P, I64, P, P, SZ, P]
     lib.crisp_sparse_attn.argtypes = [ps, pc, P, P, P, P, P, I64, P, I, P, SZ, P]
     lib.dense_attn.argtypes = [ps, P, P, P, P, I, P, SZ, P]
+    lib.flex_route.argtypes = [ps, pc, ctypes.c_float, P, P, P, P, P, P, SZ, P]
+    lib.flex_select.argtypes = [ps, pc, P, P, P, P, P, P, P, I64, P, P, SZ, P]
     lib.crisp_status_string.argtypes = [I]
     lib.crisp_status_string.restype = ctypes.c_char_p
     lib.crisp_last_error.restype = ctypes.c_char_p
     for f in ("crisp_workspace_bytes", "crisp_max_blocks", "crisp_use_dense", "crisp_route", "crisp_select",
-              "crisp_sparse_attn", "dense_attn"):
+              "crisp_sparse_attn", "dense_attn", "flex_route", "flex_select"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -169,7 +172,7 @@ def route(q, k, cfg: Cfg | None = None, out: dict | None = None, ws=None, stream
 
 
 def select(q, k, routed: dict, cfg: Cfg | None = None, out: dict | None = None, ws=None,
-           with_mask: bool = False, stream=None) -> dict:
+           with_mask: bool = False, stream=None, _flex: bool = False) -> dict:
     """VSIndex / PEIndex: the selected block set as a CSR over (batch, head, query block)."""
     import torch
     cfg = cfg or config()
@@ -183,13 +186,41 @@ def select(q, k, routed: dict, cfg: Cfg | None = None, out: dict | None = None, 
                    col_idx=torch.empty(max(cap, 1), dtype=torch.int32, device=dev))
         if with_mask:
             out["sel_mask"] = torch.empty(bh, 2, nb, dtype=torch.uint8, device=dev)
-    nws = workspace_bytes(sh, cfg, CALL_SELECT)
+    nws = workspace_bytes(sh, cfg, CALL_FLEX_SELECT if _flex else CALL_SELECT)
     ws = _workspace(nws, dev, ws)
-    _check(load().crisp_select(ctypes.byref(sh), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(routed["pattern"]),
+    fn = load().flex_select if _flex else load().crisp_select
+    _check(fn(ctypes.byref(sh), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(routed["pattern"]),
                                _ptr(routed["p_vert"]), _ptr(routed["p_slash"]), _ptr(out["row_ptr"]),
                                _ptr(out["col_idx"]), out["col_idx"].numel(), _ptr(out.get("sel_mask")),
                                _ptr(ws), nws, _stream(stream)))
     return out
+
+
+def flex_route(q, k, routed: dict, tau_jsd: float = 0.1, cfg: Cfg | None = None, out: dict | None = None, ws=None,
+               stream=None) -> dict:
+    """FlexPrefill's router: D_JS between the proxy's block distribution (routed['p_vert'],
+    from route()) and the pooled estimate; VS iff D_JS >= tau_jsd.  Returns jsd, pattern and
+    the p_vert / p_slash it was given (the input of flex_select)."""
+    import torch
+    cfg = cfg or config()
+    _check_qkv(q, k)
+    sh = shape_of(q, k)
+    bh = sh.batch * sh.h_q
+    dev = q.device
+    out = out or dict(jsd=torch.empty(bh, dtype=torch.float32, device=dev),
+                      pattern=torch.empty(bh, dtype=torch.int8, device=dev))
+    nws = workspace_bytes(sh, cfg, CALL_FLEX_ROUTE)
+    ws = _workspace(nws, dev, ws)
+    _check(load().flex_route(ctypes.byref(sh), ctypes.byref(cfg), ctypes.c_float(tau_jsd), _ptr(q), _ptr(k),
+                             _ptr(routed["p_vert"]), _ptr(out["jsd"]), _ptr(out["pattern"]), _ptr(ws), nws,
+                             _stream(stream)))
+    return dict(out, p_vert=routed["p_vert"], p_slash=routed["p_slash"])
+
+
+def flex_select(q, k, froute: dict, cfg: Cfg | None = None, out: dict | None = None, ws=None,
+                with_mask: bool = False, stream=None) -> dict:
+    """FlexPrefill's index selection (gamma-cumsum VS budget, the same PEIndex) as a block CSR."""
+    return select(q, k, froute, cfg, out=out, ws=ws, with_mask=with_mask, stream=stream, _flex=True)
 
 
 def sparse_attn(q, k, v, sel: dict, cfg: Cfg | None = None, out=None, out_dtype=None, ws=None,
@@ -241,3 +272,14 @@ def prefill(q, k, v, cfg: Cfg | None = None, out_dtype=None, stream=None, gate: 
     s = select(q, k, r, cfg, stream=stream)
     o = sparse_attn(q, k, v, s, cfg, out_dtype=out_dtype, stream=stream)
     return dict(route=r, select=s, out=o, path="sparse")
+
+
+def flex_prefill(q, k, v, cfg: Cfg | None = None, tau_jsd: float = 0.1, out_dtype=None, stream=None) -> dict:
+    """The FlexPrefill baseline on one layer: proxy, JSD routing, gamma-cumsum VS / PE selection,
+    the same sparse attention."""
+    cfg = cfg or config()
+    r = route(q, k, cfg, stream=stream)
+    f = flex_route(q, k, r, tau_jsd, cfg, stream=stream)
+    s = flex_select(q, k, f, cfg, stream=stream)
+    o = sparse_attn(q, k, v, s, cfg, out_dtype=out_dtype, stream=stream)
+    return dict(route=r, flex_route=f, select=s, out=o)

@@ -84,6 +84,8 @@ size_t ws_bytes_for(const Dims& dm, int call) {
     case CRISP_CALL_SELECT: return crisp::select_ws_layout(dm, nullptr, nullptr);
     case CRISP_CALL_ATTN: return crisp::attn_ws_bytes(dm);
     case CRISP_CALL_DENSE: return crisp::attn_ws_bytes(dm);
+    case CRISP_CALL_FLEX_ROUTE: return crisp::flex_route_ws_bytes(dm);
+    case CRISP_CALL_FLEX_SELECT: return crisp::select_ws_layout(dm, nullptr, nullptr);
     default: return (size_t)-1;
   }
 }
@@ -147,10 +149,10 @@ int crisp_route(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf
                                         w.part, w.stats, w.lu, static_cast<hipStream_t>(stream)));
 }
 
-int crisp_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
-                 const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
-                 int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws, size_t ws_bytes,
-                 void* stream) {
+static int select_common(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
+                         const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
+                         int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws, size_t ws_bytes,
+                         void* stream, int vs_rule) {
   Dims dm;
   int st = make_dims(shape, &dm);
   if (st) return st;
@@ -167,7 +169,42 @@ int crisp_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_b
   return hip_status(crisp::launch_select(dm, cfg->alpha, cfg->gamma, cfg->k_min_tokens / kBlock,
                                          static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(k_bf16),
                                          pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask, w,
-                                         static_cast<hipStream_t>(stream)));
+                                         static_cast<hipStream_t>(stream), vs_rule));
+}
+
+int crisp_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
+                 const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
+                 int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws, size_t ws_bytes,
+                 void* stream) {
+  return select_common(shape, cfg, q_bf16, k_bf16, pattern, p_vert, p_slash, row_ptr, col_idx, col_capacity,
+                       sel_mask, ws, ws_bytes, stream, crisp::VS_NOISE_FLOOR);
+}
+
+int flex_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
+                const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
+                int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws, size_t ws_bytes,
+                void* stream) {
+  return select_common(shape, cfg, q_bf16, k_bf16, pattern, p_vert, p_slash, row_ptr, col_idx, col_capacity,
+                       sel_mask, ws, ws_bytes, stream, crisp::VS_GAMMA_CUMSUM);
+}
+
+int flex_route(const crisp_shape* shape, const crisp_cfg* cfg, float tau_jsd, const void* q_bf16,
+               const void* k_bf16, const float* p_vert, float* jsd, int8_t* pattern, void* ws, size_t ws_bytes,
+               void* stream) {
+  Dims dm;
+  int st = make_dims(shape, &dm);
+  if (st) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if (!(tau_jsd >= 0.f) || !std::isfinite(tau_jsd)) return CRISP_ERR_PARAM;
+  if (dm.batch == 0) return CRISP_OK;
+  if (!q_bf16 || !k_bf16 || !p_vert || !jsd || !pattern || !ws) return CRISP_ERR_NULL;
+  if (misaligned(q_bf16) || misaligned(k_bf16) || misaligned(p_vert) || misaligned(jsd) || misaligned(pattern) ||
+      misaligned(ws))
+    return CRISP_ERR_ALIGN;
+  if (ws_bytes < crisp::flex_route_ws_bytes(dm)) return CRISP_ERR_WORKSPACE;
+  return hip_status(crisp::launch_flex_route(dm, tau_jsd, static_cast<const uint16_t*>(q_bf16),
+                                             static_cast<const uint16_t*>(k_bf16), p_vert, jsd, pattern,
+                                             static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
 }
 
 int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,

@@ -39,10 +39,21 @@ struct SelectWs {
   int64_t* scan_part;   // [scan blocks + 1]
 };
 size_t select_ws_layout(const Dims& dm, SelectWs* ws, char* base);
+// vs_rule: VS_NOISE_FLOOR (CRISP's VSIndex) or VS_GAMMA_CUMSUM (FlexPrefill's budget rule)
+enum { VS_NOISE_FLOOR = 0, VS_GAMMA_CUMSUM = 1 };
 hipError_t launch_select(const Dims& dm, float alpha, float gamma, int kmin_blocks,
                          const uint16_t* q, const uint16_t* k, const int8_t* pattern,
                          const float* p_vert, const float* p_slash, int64_t* row_ptr,
-                         int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st);
+                         int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st,
+                         int vs_rule = VS_NOISE_FLOOR);
+
+// ---- the FlexPrefill baseline path (flex.hip) ----
+// ws: flex_route_ws_bytes(dm) bytes (pooled keys of every KV group)
+size_t flex_route_ws_bytes(const Dims& dm);
+hipError_t launch_flex_route(const Dims& dm, float tau, const uint16_t* q, const uint16_t* k, const float* p_vert,
+                             float* jsd, int8_t* pattern, float* kbar, hipStream_t st);
+hipError_t launch_flex_vs(const Dims& dm, float gamma, int kmin_blocks, const int8_t* pattern, const float* p_vert,
+                          const float* p_slash, uint8_t* vsflags, uint8_t* sel_mask, hipStream_t st);
 
 // ---- attention (attn.hip) ----
 // ws: attn_ws_bytes(dm) bytes of scratch (work-queue counters and a V^T copy)

@@ -575,10 +575,15 @@ __global__ __launch_bounds__(64) void fill_kernel(const int8_t* __restrict__ pat
 template <int D>
 hipError_t select_impl(const Dims& dm, float alpha, float gamma, int kmin, const uint16_t* q, const uint16_t* k,
                        const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
-                       int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st) {
+                       int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st, int vs_rule) {
   const int nb = dm.nb;
   const unsigned bh = (unsigned)dm.bh;
-  vs_select_kernel<<<bh, NTHR, 0, st>>>(pattern, p_vert, p_slash, ws.vsflags, sel_mask, nb, alpha, kmin);
+  if (vs_rule == VS_GAMMA_CUMSUM) {
+    const hipError_t e = launch_flex_vs(dm, gamma, kmin, pattern, p_vert, p_slash, ws.vsflags, sel_mask, st);
+    if (e != hipSuccess) return e;
+  } else {
+    vs_select_kernel<<<bh, NTHR, 0, st>>>(pattern, p_vert, p_slash, ws.vsflags, sel_mask, nb, alpha, kmin);
+  }
   pool_q_kernel<D><<<dim3(nb, bh), NTHR, 0, st>>>(q, pattern, ws.qbar, dm.n);
   pool_k_kernel<D><<<dim3(nb, (unsigned)(dm.batch * dm.h_kv)), NTHR, 0, st>>>(k, pattern, ws.kbar, dm.n, dm.h_q, dm.group);
   const int tiles = (nb + 63) / 64;
@@ -636,10 +641,12 @@ size_t select_ws_layout(const Dims& dm, SelectWs* ws, char* base) {
 
 hipError_t launch_select(const Dims& dm, float alpha, float gamma, int kmin_blocks, const uint16_t* q, const uint16_t* k,
                          const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
-                         int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st) {
+                         int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st, int vs_rule) {
   if (dm.d == 128)
-    return select_impl<128>(dm, alpha, gamma, kmin_blocks, q, k, pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask, ws, st);
-  return select_impl<64>(dm, alpha, gamma, kmin_blocks, q, k, pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask, ws, st);
+    return select_impl<128>(dm, alpha, gamma, kmin_blocks, q, k, pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask,
+                            ws, st, vs_rule);
+  return select_impl<64>(dm, alpha, gamma, kmin_blocks, q, k, pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask, ws,
+                         st, vs_rule);
 }
 
 }  // namespace crisp

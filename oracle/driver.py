@@ -59,6 +59,27 @@ def layer_selection(q_bits, k_bits, *, tau=0.2, alpha=1.0, gamma=0.95, k_min_tok
             return dict(ex.map(one, todo))
 
 
+def layer_selection_flex(q_bits, k_bits, *, tau_jsd=0.1, gamma=0.95, k_min_tokens=1024,
+                         heads=None, force_vs=None, workers=None):
+    """FlexPrefill's routing and selection (flex_head) of every (batch, head) pair of one layer."""
+    B, H = q_bits.shape[:2]
+    G = H // k_bits.shape[1]
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    force_vs = force_vs or {}
+
+    def one(bh):
+        b, h = bh
+        q = co.bf16_to_f64(q_bits[b, h])
+        k = co.bf16_to_f64(k_bits[b, h // G])
+        return bh, co.flex_head(q, k, tau_jsd=tau_jsd, gamma=gamma, k_min_tokens=k_min_tokens,
+                                force_vs=force_vs.get(bh))
+
+    workers = workers or default_workers()
+    with _blas_limit(1):
+        with ThreadPoolExecutor(min(workers, len(todo)) or 1) as ex:
+            return dict(ex.map(one, todo))
+
+
 def layer_attention(q_bits, k_bits, v_bits, rows_of, blocks_of, *, workers=None, q_rows=None):
     """Exact block-sparse attention on chosen query blocks.
 

@@ -128,6 +128,33 @@ def test_select_rejects_before_any_hip_call(lib):
     assert call(cap, need, rp=None) == NULL
 
 
+def test_flex_calls_reject_before_any_hip_call(lib):
+    sh, cfg = shape(), crisp.config()
+    need_r = crisp.workspace_bytes(sh, cfg, crisp.CALL_FLEX_ROUTE)
+    need_s = crisp.workspace_bytes(sh, cfg, crisp.CALL_FLEX_SELECT)
+    assert need_r == 1 * 2 * (4096 // 128) * 64 * 4          # pooled keys of every KV group, fp32
+    assert need_s == crisp.workspace_bytes(sh, cfg, crisp.CALL_SELECT)
+
+    def route(tau=0.1, ws_bytes=need_r, ptrs=None, sh_=sh):
+        ptrs = ptrs or [FAKE] * 6
+        return lib.flex_route(ctypes.byref(sh_), ctypes.byref(cfg), ctypes.c_float(tau), *ptrs, ws_bytes, None)
+    for bad in (-0.1, float("nan"), float("inf")):
+        assert route(tau=bad) == PARAM
+    assert route(ws_bytes=need_r - 1) == WS
+    assert route(ptrs=[FAKE, FAKE, None, FAKE, FAKE, FAKE]) == NULL
+    assert route(ptrs=[FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE]) == ALIGN
+    assert route(sh_=shape(n=1000)) == SHAPE
+    assert route(sh_=shape(batch=0), ptrs=[None] * 6, ws_bytes=0) == OK
+    cap = crisp.max_blocks(sh)
+
+    def select(cap_, ws_bytes, rp=FAKE):
+        return lib.flex_select(ctypes.byref(sh), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, rp, FAKE,
+                               cap_, None, FAKE, ws_bytes, None)
+    assert select(cap - 1, need_s) == CAP
+    assert select(cap, need_s - 1) == WS
+    assert select(cap, need_s, rp=None) == NULL
+
+
 def test_attention_rejects_before_any_hip_call(lib):
     sh, cfg = shape(), crisp.config()
     need = crisp.workspace_bytes(sh, cfg, 2)
