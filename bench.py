@@ -49,6 +49,11 @@ def parse():
                     help="measured HBM bytes per attention launch (JSON), if current")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a device copy of this many MiB (HBM counter calibration) and exit")
+    ap.add_argument("--model-sweep", type=int, default=0, metavar="LAYERS",
+                    help="only sum CRISP, FlexPrefill and dense attention over this many Llama-3.1-8B-shaped "
+                         "layers (distinct seeds) at 64k, 128k, 256k and 512k tokens")
+    ap.add_argument("--sweep-lengths", default="65536,131072,262144,524288")
+    ap.add_argument("--sweep-n-vert", type=int, default=64, help="planted vertical keys per KV group in the sweep")
     ap.add_argument("--crossover", action="store_true",
                     help="only sweep the sequence length (Llama-shaped layers, 4k-128k) and report where the "
                          "sparse path overtakes dense attention")
@@ -294,6 +299,44 @@ def crossover_workload(n):
                     seed=9000 + n.bit_length())
 
 
+def sweep_workload(n, layer, n_vert=64):
+    """Layer `layer` of a Llama-3.1-8B-shaped model at n tokens: the recipe of the 128k and
+    512k layers (75% VS heads, sink scale 3, 64 planted vertical keys per KV group)."""
+    from prefill_inputs import Shape, Workload
+    return Workload(name=f"llama3_8b_model_n{n}_layer{layer}", shape=Shape(1, n, 32, 8, 128), vs_fraction=0.75,
+                    sink_scale=3.0, n_vert=n_vert, alphas=(1.0,), seed=20000 + 100 * n.bit_length() + layer)
+
+
+def model_sweep(args):
+    """Attention-only whole-model totals: sum over the layers of one prefill."""
+    rows = []
+    for n in [int(x) for x in args.sweep_lengths.split(",") if x]:
+        tot = dict(crisp=0.0, flex=0.0, tiles=0, flex_tiles=0)
+        dense_ms = None
+        for L in range(args.model_sweep):
+            layer = Layer(sweep_workload(n, L, args.sweep_n_vert))
+            r = layer.measure(1.0, 2, 1)
+            f = layer.measure_flex(1.0, args.tau_jsd, 2, 1)
+            if dense_ms is None:
+                dense_ms, _ = layer.dense(max(1, args.dense_steps))
+            tot["crisp"] += r["ms_per_layer"]
+            tot["flex"] += f["ms_per_layer"]
+            tot["tiles"] += r["tiles"]
+            tot["flex_tiles"] += f["tiles"]
+            log(f"[sweep] n={n} layer {L}: CRISP {r['ms_per_layer']:.2f} ms, FlexPrefill {f['ms_per_layer']:.2f} ms")
+            layer.free()
+        L = args.model_sweep
+        rows.append(dict(n=n, layers=L, crisp_ms=round(tot["crisp"], 1), flex_ms=round(tot["flex"], 1),
+                         dense_ms=round(dense_ms * L, 1), crisp_vs_dense=round(dense_ms * L / tot["crisp"], 3),
+                         flex_vs_dense=round(dense_ms * L / tot["flex"], 3),
+                         crisp_vs_flex=round(tot["flex"] / tot["crisp"], 3), tiles=tot["tiles"],
+                         flex_tiles=tot["flex_tiles"]))
+        log(f"[sweep] n={n}: {rows[-1]}")
+    print(json.dumps({"model_sweep": rows, "model": "Llama-3.1-8B-shaped, 32/8 heads, d=128, attention only",
+                      "n_vert": args.sweep_n_vert,
+                      "dense": "one layer's dense time x layers (dense time depends only on the shape)"}))
+
+
 def crossover(args):
     """Sparse layer (route + select + attention) vs dense attention over n."""
     rows = []
@@ -333,6 +376,9 @@ def main():
 
     if args.crossover:
         crossover(args)
+        return
+    if args.model_sweep:
+        model_sweep(args)
         return
 
     idx = ALIASES.get(args.workload) or int(args.workload)
