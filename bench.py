@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="llama512k", help="|".join(ALIASES))
     ap.add_argument("--alpha", type=float, default=None, help="default: the workload's first setting")
-    ap.add_argument("--also", default="llama512k@1.25,llama128k,llama128k@1.25",
+    ap.add_argument("--also", default="llama512k@1.25,llama512k@1.5,llama128k,llama128k@1.25",
                     help="extra workload[@alpha] list reported under 'also' ('' = none)")
     ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-dense", action="store_true")

@@ -53,6 +53,12 @@ R18 FlexPrefill's JSD router (the method CRISP replaces): a_hat is the proxy's
     over all N_b blocks (the last query block sees every key block).  D_JS uses
     the natural log; the head routes VS iff D_JS >= tau_jsd.  The pages give
     no value for tau_jsd; it is a parameter.
+R20 Median noise floor (the variant of the pages' Table 9): mu is the median
+    of the N_b-2 non-anchor block scores instead of their mean; the rest of the
+    rule is unchanged.
+R21 Slash band (variant of R6): a selected slash block covers the token
+    offsets 128 delta .. 128 delta + 127, which fall in the tiles of block
+    diagonals delta and delta + 1, so both are selected.
 R19 FlexPrefill's VS index is Algorithm 3 with the per-direction noise-floor
     rule replaced by the gamma-cumsum budget rule (same gamma as the PE path):
     the shortest descending prefix of p_d reaching gamma, its count clipped to
@@ -137,18 +143,21 @@ def vs_scores(a_hat: np.ndarray, block: int = BLOCK):
     return p_v, p_s
 
 
-def noise_floor_select(p: np.ndarray, alpha: float, k_min_blocks: int):
+def noise_floor_select(p: np.ndarray, alpha: float, k_min_blocks: int, floor: str = "mean"):
     """Sink-aware noise-floor selection for one direction.
 
     r = max(1 - p[0] - p[N_b-1], 0), mu = r / (N_b - 2); keep every block with
     p[j] > alpha*mu, clip the count to [k_min, N_b] (top-k, ties to the lower
     index), then add the anchor blocks 0 and N_b-1.  [digest] sections "Core
     method" and "Method steps" step 2, Algorithm 3 caption; readings R8-R10.
+    ``floor="median"`` takes mu as the median of the non-anchor scores (R20).
     Returns (sorted selected blocks, mu, number above the floor).
     """
     nb = len(p)
     r = max(1.0 - p[0] - p[nb - 1], 0.0)
     mu = r / (nb - 2)
+    if floor == "median":
+        mu = float(np.median(p[1:nb - 1]))
     above = int(np.count_nonzero(p > alpha * mu))
     k = min(max(above, k_min_blocks), nb)
     order = np.lexsort((np.arange(nb), -p))
@@ -156,12 +165,15 @@ def noise_floor_select(p: np.ndarray, alpha: float, k_min_blocks: int):
     return np.array(sorted(sel), dtype=np.int64), mu, above
 
 
-def vs_rows(sel_v: np.ndarray, sel_s: np.ndarray, nb: int):
+def vs_rows(sel_v: np.ndarray, sel_s: np.ndarray, nb: int, band: bool = False):
     """Key blocks of every query block of a VS head (R6, R7).
 
-    Row qb = {kb in S_v : kb <= qb} U {qb - delta : delta = N_b-1-k, k in S_s, delta <= qb}.
+    Row qb = {kb in S_v : kb <= qb} U {qb - delta : delta = N_b-1-k, k in S_s, delta <= qb};
+    with ``band`` the diagonals delta + 1 join as well (R21).
     """
     deltas = nb - 1 - np.asarray(sel_s)
+    if band:
+        deltas = np.union1d(deltas, deltas + 1)
     rows = []
     for qb in range(nb):
         v = sel_v[sel_v <= qb]
@@ -284,13 +296,14 @@ def dense_attention(q_h, k_g, v_g, q_blocks=None, block: int = BLOCK, q_rows=Non
 # Algorithm 1: one head end to end
 # ----------------------------------------------------------------------------
 def crisp_head(q_h, k_g, *, tau=0.2, alpha=1.0, gamma=0.95, k_min_tokens=1024,
-               block=BLOCK, force_vs=None):
+               block=BLOCK, force_vs=None, floor="mean", band=False):
     """Routing and selection of one query head, as Algorithm 1 assembles them.
 
     PatSearch, then VSIndex if the head routes VS, else PEIndex.  ``force_vs``
     overrides the routing decision (used to re-run a head whose structural mass
-    sits on the threshold).  Returns a dict with the route, the scores and the
-    per-query-block key-block rows.
+    sits on the threshold); ``floor`` and ``band`` select the variants R20 and
+    R21.  Returns a dict with the route, the scores and the per-query-block
+    key-block rows.
     """
     n = q_h.shape[0]
     nb = n // block
@@ -302,10 +315,10 @@ def crisp_head(q_h, k_g, *, tau=0.2, alpha=1.0, gamma=0.95, k_min_tokens=1024,
     res = dict(c_struct=c, is_vs=is_vs, p_v=p_v, p_s=p_s)
     if is_vs:
         kmin = k_min_tokens // block
-        sv, mu_v, cnt_v = noise_floor_select(p_v, alpha, kmin)
-        ss, mu_s, cnt_s = noise_floor_select(p_s, alpha, kmin)
+        sv, mu_v, cnt_v = noise_floor_select(p_v, alpha, kmin, floor)
+        ss, mu_s, cnt_s = noise_floor_select(p_s, alpha, kmin, floor)
         res.update(sel_v=sv, sel_s=ss, mu_v=mu_v, mu_s=mu_s, cnt_v=cnt_v, cnt_s=cnt_s,
-                   rows=vs_rows(sv, ss, nb))
+                   rows=vs_rows(sv, ss, nb, band))
     else:
         pe = pe_select(pooled_map(q_h, k_g, block), gamma)
         res.update(pe=pe, rows=pe["rows"])

@@ -407,3 +407,46 @@ def check_flex_routes_planted(co):
     planted = set((np.asarray(inp["planted"][0][0]["vert"]) // B).tolist())
     assert len(planted) > 0
     assert 0 in r0["sel_v"].tolist() and planted <= set(r0["sel_v"].tolist())
+
+
+# --- variants -----------------------------------------------------------------------
+def check_median_floor(co, seed=30):
+    """The median floor is the median of the non-anchor scores (statistics.median),
+    equals the mean floor when those scores are all equal, and then keeps what
+    the mean floor keeps."""
+    import statistics
+    rng = np.random.default_rng(seed)
+    for nb in (7, 8, 33):
+        p = rng.random(nb) ** 2
+        p /= p.sum()
+        _, mu, cnt = co.noise_floor_select(p, 1.0, 0, floor="median")
+        med = statistics.median(p[1:nb - 1].tolist())
+        assert math.isclose(mu, med, rel_tol=1e-12)
+        assert cnt == sum(1 for x in p if x > med)
+    nb = 10
+    p = np.full(nb, 0.05)
+    p[0], p[nb - 1] = 0.4 - 0.05, 0.6 - 0.4 + 0.05   # anchors hold the rest; non-anchors equal
+    p /= p.sum()
+    a = co.noise_floor_select(p, 0.9, 2, floor="median")
+    b = co.noise_floor_select(p, 0.9, 2, floor="mean")
+    assert math.isclose(a[1], b[1], rel_tol=1e-12) and a[0].tolist() == b[0].tolist()
+
+
+def check_slash_band_tokens(co):
+    """With the band, tile (qb, kb) of a VS row is selected by the slash part
+    exactly when some causal token pair of the tile has its offset inside a
+    selected slash block's 128-token range (brute force over tokens)."""
+    nb = 6
+    n = nb * B
+    sel_s = np.array([nb - 1, nb - 3])            # deltas 0 and 2
+    rows = co.vs_rows(np.array([], dtype=np.int64), sel_s, nb, band=True)
+    deltas = nb - 1 - sel_s
+    q = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    off = q - j
+    covered = (off >= 0) & np.isin(off // B, deltas)
+    tiles = covered.reshape(nb, B, nb, B).any(axis=(1, 3))
+    for qb in range(nb):
+        assert rows[qb].tolist() == np.nonzero(tiles[qb])[0].tolist(), qb
+    plain = co.vs_rows(np.array([], dtype=np.int64), sel_s, nb)
+    assert all(set(a.tolist()) <= set(b.tolist()) for a, b in zip(plain, rows))

@@ -78,3 +78,34 @@ def test_layer_parity(idx, alpha):
         _log(f"[{wl.name}] dense ok: max-abs {worst:.2e} mean-abs {mean:.2e}")
         del dense
     del g
+
+
+# The pages' variant settings on the same kernels: alpha = 1.5 (their fastest
+# setting at 512k) and the routing thresholds tau = 0.15 and 0.25 of their
+# sensitivity study.  Routing and selection in full, outputs on sampled blocks.
+VARIANTS = [(3, 1.5, None), (2, 1.0, 0.15), (2, 1.0, 0.25)]
+
+
+@pytest.mark.parametrize("idx,alpha,tau", VARIANTS,
+                         ids=[f"{WORKLOADS[i].name}-alpha{a}-tau{t}" for i, a, t in VARIANTS])
+def test_variant_settings(idx, alpha, tau):
+    st = _state(idx)
+    wl, inp = st["wl"], st["inp"]
+    sh = wl.shape
+    nb = sh.n_blocks
+    cfg = crisp.config(tau=wl.tau if tau is None else tau, alpha=alpha, gamma=wl.gamma,
+                       k_min_tokens=wl.k_min_tokens)
+    ckw = cfg_kwargs(cfg)
+    q, k, v = st["dev"]
+    g = gpu_layer(q, k, v, cfg)
+    check_csr_structure(g, sh.batch * sh.h_q, nb, crisp.max_blocks(crisp.shape_of(q, k)))
+    ora = oracle_layer(inp, ckw)
+    ora, stats = check_selection(g, inp, ora, ckw, sh.h_q, nb)
+    _log(f"[{wl.name} alpha={alpha} tau={ckw['tau']}] selection ok: tiles={int(g['row_ptr'][-1])} "
+         f"vs={int(g['pattern'].sum())} diffs={stats}")
+    rng = np.random.default_rng(idx * 7 + int(alpha * 10))
+    blocks = {bh: sample_blocks(nb, rng) for bh in ora}
+    rows = {bh: rows_of(g, bh[0] * sh.h_q + bh[1], nb) for bh in ora}
+    worst, mean = check_outputs(g["out"], inp, rows, blocks)
+    _log(f"[{wl.name} alpha={alpha} tau={ckw['tau']}] outputs ok: max-abs {worst:.2e} mean-abs {mean:.2e}")
+    del g

@@ -42,6 +42,8 @@ MUTANTS = {
     "pooled_est_no_scale": ("    s = (kbar @ qbar) / math.sqrt(d)", "    s = (kbar @ qbar)"),
     "flex_no_kmin": ("    k = min(max(len(kept), k_min_blocks), nb)", "    k = min(len(kept), nb)"),
     "flex_no_anchors": ("    sel = {0, nb - 1}.union(order[:k].tolist())", "    sel = set(order[:k].tolist())"),
+    "median_with_anchors": ("        mu = float(np.median(p[1:nb - 1]))", "        mu = float(np.median(p))"),
+    "band_wrong_side": ("        deltas = np.union1d(deltas, deltas + 1)", "        deltas = np.union1d(deltas, deltas - 1)"),
     "bf16_decode_shift": ("    w = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)",
                           "    w = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)"),
 }
