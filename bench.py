@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flex", action="store_true", help="skip the FlexPrefill baseline path")
+    ap.add_argument("--no-variants", action="store_true", help="skip the VSIndex variants (median floor, slash band)")
     ap.add_argument("--tau-jsd", type=float, default=0.1, help="JSD threshold of the FlexPrefill router")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per attention launch (JSON), if current")
@@ -102,31 +103,31 @@ class Layer:
         wl = self.wl
         return self.crisp.config(tau=wl.tau, alpha=alpha, gamma=wl.gamma, k_min_tokens=wl.k_min_tokens)
 
-    def step(self, cfg, evs=None):
+    def step(self, cfg, evs=None, variant=0):
         c = self.crisp
         if evs:
             evs[0].record()
         c.route(self.q, self.k, cfg, out=self.r_out, ws=self.ws_r)
         if evs:
             evs[1].record()
-        c.select(self.q, self.k, self.r_out, cfg, out=self.s_out, ws=self.ws_s)
+        c.select(self.q, self.k, self.r_out, cfg, out=self.s_out, ws=self.ws_s, variant=variant)
         if evs:
             evs[2].record()
         c.sparse_attn(self.q, self.k, self.v, self.s_out, cfg, out=self.o)
         if evs:
             evs[3].record()
 
-    def measure(self, alpha, steps, warmup):
+    def measure(self, alpha, steps, warmup, variant=0):
         import torch
         cfg = self.cfg(alpha)
         for _ in range(warmup):
-            self.step(cfg)
+            self.step(cfg, variant=variant)
         torch.cuda.synchronize()
         evs = [[_event() for _ in range(4)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.step(cfg, evs[i])
+            self.step(cfg, evs[i], variant=variant)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
         st = dict(route=0.0, select=0.0, attn=0.0)
@@ -390,7 +391,7 @@ def main():
     for j, _ in specs:
         if j not in order:
             order.append(j)
-    results, dense, keep, flex = [], {}, None, []
+    results, dense, keep, flex, variants = [], {}, None, [], []
     for j in order:
         layer = Layer(j)
         for jj, a in specs:
@@ -407,6 +408,15 @@ def main():
             if r["_primary"]:
                 rp, col = layer.host_csr()
                 keep = (layer, rp, col, r)
+                if not args.no_variants:
+                    c = layer.crisp
+                    for nm, bits in (("median_floor", c.VARIANT_MEDIAN_FLOOR), ("slash_band", c.VARIANT_SLASH_BAND)):
+                        vr = layer.measure(a, 2, 1, variant=bits)
+                        variants.append(dict(variant=nm, workload=vr["workload"], alpha=a,
+                                             ms_per_layer=round(vr["ms_per_layer"], 3), stage_ms=vr["stage_ms"],
+                                             tiles=vr["tiles"]))
+                        log(f"[bench] {vr['workload']} variant {nm}: {vr['ms_per_layer']:.2f} ms/layer "
+                            f"tiles={vr['tiles']}")
         if not args.no_flex:
             a0 = next(a for jj, a in specs if jj == j)
             a0 = layer.wl.alphas[0] if a0 is None else a0
@@ -480,6 +490,8 @@ def main():
     out["selection_gbs"] = stage_rates(sh, res)
     if flex:
         out["flexprefill"] = flex
+    if variants:
+        out["variants"] = variants
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(layer, res, rp, col)

@@ -168,6 +168,21 @@ int dense_attn(const crisp_shape* shape, const void* q_bf16, const void* k_bf16,
                const void* v_bf16, void* out, int out_dtype, void* ws, size_t ws_bytes,
                void* stream);
 
+/* Variants of VSIndex on the same kernels (bits of `variant`):
+ * CRISP_VARIANT_MEDIAN_FLOOR: mu = the median of the N_b - 2 non-anchor
+ *   block scores instead of their mean (the digest's limitations and
+ *   weakness notes, Table 9); the rest of the rule is unchanged.
+ * CRISP_VARIANT_SLASH_BAND: a selected slash block covers the token offsets
+ *   128 delta .. 128 delta + 127, which reach the tiles of block diagonals
+ *   delta and delta + 1; both are selected (the default selects delta only).
+ * Everything else (arguments, workspace CRISP_CALL_SELECT, errors) is as for
+ * crisp_select; unknown bits give CRISP_ERR_PARAM. */
+enum crisp_variant { CRISP_VARIANT_MEDIAN_FLOOR = 1, CRISP_VARIANT_SLASH_BAND = 2 };
+int crisp_select_variant(const crisp_shape* shape, const crisp_cfg* cfg, int variant, const void* q_bf16,
+                         const void* k_bf16, const int8_t* pattern, const float* p_vert, const float* p_slash,
+                         int64_t* row_ptr, int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* The FlexPrefill baseline: the routing and VS budget rule that CRISP
  * replaces, on the same kernels (digest: prerequisite sections on
  * Jensen-Shannon divergence and on the cumulative-coverage threshold).

@@ -28,6 +28,7 @@ _LIB_PATH = os.path.join(_HERE, "libcrisp.so")
 _lib = None
 
 CALL_ROUTE, CALL_SELECT, CALL_ATTN, CALL_DENSE, CALL_FLEX_ROUTE, CALL_FLEX_SELECT = 0, 1, 2, 3, 4, 5
+VARIANT_MEDIAN_FLOOR, VARIANT_SLASH_BAND = 1, 2
 OUT_F32, OUT_BF16 = 0, 1
 
 
@@ -72,11 +73,12 @@ def load():
     lib.dense_attn.argtypes = [ps, P, P, P, P, I, P, SZ, P]
     lib.flex_route.argtypes = [ps, pc, ctypes.c_float, P, P, P, P, P, P, SZ, P]
     lib.flex_select.argtypes = [ps, pc, P, P, P, P, P, P, P, I64, P, P, SZ, P]
+    lib.crisp_select_variant.argtypes = [ps, pc, I, P, P, P, P, P, P, P, I64, P, P, SZ, P]
     lib.crisp_status_string.argtypes = [I]
     lib.crisp_status_string.restype = ctypes.c_char_p
     lib.crisp_last_error.restype = ctypes.c_char_p
     for f in ("crisp_workspace_bytes", "crisp_max_blocks", "crisp_use_dense", "crisp_route", "crisp_select",
-              "crisp_sparse_attn", "dense_attn", "flex_route", "flex_select"):
+              "crisp_sparse_attn", "dense_attn", "flex_route", "flex_select", "crisp_select_variant"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -172,8 +174,10 @@ def route(q, k, cfg: Cfg | None = None, out: dict | None = None, ws=None, stream
 
 
 def select(q, k, routed: dict, cfg: Cfg | None = None, out: dict | None = None, ws=None,
-           with_mask: bool = False, stream=None, _flex: bool = False) -> dict:
-    """VSIndex / PEIndex: the selected block set as a CSR over (batch, head, query block)."""
+           with_mask: bool = False, stream=None, _flex: bool = False, variant: int = 0) -> dict:
+    """VSIndex / PEIndex: the selected block set as a CSR over (batch, head, query block).
+
+    ``variant``: bits VARIANT_MEDIAN_FLOOR / VARIANT_SLASH_BAND (crisp_select_variant)."""
     import torch
     cfg = cfg or config()
     _check_qkv(q, k)
@@ -188,7 +192,11 @@ def select(q, k, routed: dict, cfg: Cfg | None = None, out: dict | None = None, 
             out["sel_mask"] = torch.empty(bh, 2, nb, dtype=torch.uint8, device=dev)
     nws = workspace_bytes(sh, cfg, CALL_FLEX_SELECT if _flex else CALL_SELECT)
     ws = _workspace(nws, dev, ws)
-    fn = load().flex_select if _flex else load().crisp_select
+    if variant:
+        lib = load()
+        fn = lambda *a: lib.crisp_select_variant(a[0], a[1], variant, *a[2:])   # noqa: E731
+    else:
+        fn = load().flex_select if _flex else load().crisp_select
     _check(fn(ctypes.byref(sh), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(routed["pattern"]),
                                _ptr(routed["p_vert"]), _ptr(routed["p_slash"]), _ptr(out["row_ptr"]),
                                _ptr(out["col_idx"]), out["col_idx"].numel(), _ptr(out.get("sel_mask")),

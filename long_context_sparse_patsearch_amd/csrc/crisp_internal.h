@@ -39,13 +39,15 @@ struct SelectWs {
   int64_t* scan_part;   // [scan blocks + 1]
 };
 size_t select_ws_layout(const Dims& dm, SelectWs* ws, char* base);
-// vs_rule: VS_NOISE_FLOOR (CRISP's VSIndex) or VS_GAMMA_CUMSUM (FlexPrefill's budget rule)
-enum { VS_NOISE_FLOOR = 0, VS_GAMMA_CUMSUM = 1 };
+// vs_rule: VS_NOISE_FLOOR (CRISP's VSIndex), VS_GAMMA_CUMSUM (FlexPrefill's budget rule) or
+// VS_MEDIAN_FLOOR (the noise floor with the median of the non-anchor scores); band: a selected
+// slash block also selects block diagonal delta + 1.
+enum { VS_NOISE_FLOOR = 0, VS_GAMMA_CUMSUM = 1, VS_MEDIAN_FLOOR = 2 };
 hipError_t launch_select(const Dims& dm, float alpha, float gamma, int kmin_blocks,
                          const uint16_t* q, const uint16_t* k, const int8_t* pattern,
                          const float* p_vert, const float* p_slash, int64_t* row_ptr,
                          int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st,
-                         int vs_rule = VS_NOISE_FLOOR);
+                         int vs_rule = VS_NOISE_FLOOR, int band = 0);
 
 // ---- the FlexPrefill baseline path (flex.hip) ----
 // ws: flex_route_ws_bytes(dm) bytes (pooled keys of every KV group)
@@ -54,6 +56,8 @@ hipError_t launch_flex_route(const Dims& dm, float tau, const uint16_t* q, const
                              float* jsd, int8_t* pattern, float* kbar, hipStream_t st);
 hipError_t launch_flex_vs(const Dims& dm, float gamma, int kmin_blocks, const int8_t* pattern, const float* p_vert,
                           const float* p_slash, uint8_t* vsflags, uint8_t* sel_mask, hipStream_t st);
+hipError_t launch_median_vs(const Dims& dm, float alpha, int kmin_blocks, const int8_t* pattern, const float* p_vert,
+                            const float* p_slash, uint8_t* vsflags, uint8_t* sel_mask, hipStream_t st);
 
 // ---- attention (attn.hip) ----
 // ws: attn_ws_bytes(dm) bytes of scratch (work-queue counters and a V^T copy)

@@ -134,6 +134,109 @@ __global__ __launch_bounds__(NTHR) void flex_route_kernel(const uint16_t* __rest
   }
 }
 
+// Bitonic sort of np (a power of two) (score, index) pairs in LDS into score
+// descending, index ascending order; every thread of the workgroup calls it.
+__device__ __forceinline__ void sort_desc(float* sv, int* si, int np) {
+  const int tid = threadIdx.x;
+  for (int kk = 2; kk <= np; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < np; i += NTHR) {
+        const int l = i ^ jj;
+        if (l > i) {
+          const float a = sv[i], c = sv[l];
+          const int ia = si[i], ic = si[l];
+          const bool l_first = c > a || (c == a && ic < ia);   // element l belongs before element i
+          const bool up = (i & kk) == 0;
+          if (up ? l_first : !l_first) {
+            sv[i] = c;
+            sv[l] = a;
+            si[i] = ic;
+            si[l] = ia;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// One workgroup per (batch, query head): VS flags of both directions by the
+// noise floor with mu = the median of the N_b - 2 non-anchor scores (the
+// variant of the digest's Table 9): keep p > alpha mu, at least k_min blocks
+// (top-k, ties to the lower index), plus the anchors (PE heads: all zero).
+__global__ __launch_bounds__(NTHR) void median_vs_kernel(const int8_t* __restrict__ pattern,
+                                                         const float* __restrict__ p_vert,
+                                                         const float* __restrict__ p_slash,
+                                                         uint8_t* __restrict__ vsflags, uint8_t* __restrict__ sel_mask,
+                                                         int nb, float alpha, int kmin) {
+  __shared__ float sv[MAX_NB];
+  __shared__ int si[MAX_NB];
+  __shared__ uint8_t fl[MAX_NB];
+  __shared__ float thr_s;
+  __shared__ int cnt_s;
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const bool vs = pattern[bh] == 1;
+  int np = 1;
+  while (np < nb) np <<= 1;
+  for (int dir = 0; dir < 2; ++dir) {
+    uint8_t* gfl = vsflags + ((size_t)bh * 2 + dir) * nb;
+    uint8_t* sm = sel_mask ? sel_mask + ((size_t)bh * 2 + dir) * nb : nullptr;
+    if (!vs) {
+      for (int j = tid; j < nb; j += NTHR) {
+        gfl[j] = 0;
+        if (sm) sm[j] = 0;
+      }
+      continue;
+    }
+    const float* p = (dir ? p_slash : p_vert) + (size_t)bh * nb;
+    for (int j = tid; j < np; j += NTHR) {
+      sv[j] = j < nb ? p[j] : -INFINITY;
+      si[j] = j < nb ? j : 0x7fffffff;
+    }
+    for (int j = tid; j < nb; j += NTHR) fl[j] = 0;
+    if (tid == 0) cnt_s = 0;
+    __syncthreads();
+    sort_desc(sv, si, np);
+    if (tid == 0) {
+      // ranks (m-1)/2 and m/2 among the non-anchor blocks, m = nb - 2, in sorted order
+      const int m = nb - 2, lo = (m - 1) / 2, hi = m / 2;
+      float vlo = 0.f, vhi = 0.f;
+      int seen = 0;
+      for (int t = 0; t < nb && seen <= hi; ++t) {
+        const int j = si[t];
+        if (j == 0 || j == nb - 1) continue;
+        if (seen == lo) vlo = sv[t];
+        if (seen == hi) vhi = sv[t];
+        ++seen;
+      }
+      const float mu = lo == hi ? vlo : 0.5f * (vlo + vhi);
+      thr_s = alpha * mu;
+    }
+    __syncthreads();
+    const float thr = thr_s;
+    int c = 0;
+    for (int j = tid; j < nb; j += NTHR) c += p[j] > thr ? 1 : 0;
+    atomicAdd(&cnt_s, c);
+    __syncthreads();
+    int take = cnt_s > kmin ? cnt_s : kmin;
+    if (take > nb) take = nb;
+    for (int t = tid; t < take; t += NTHR)
+      if (si[t] < nb) fl[si[t]] = 1;
+    __syncthreads();
+    if (tid == 0) {
+      fl[0] = 1;
+      fl[nb - 1] = 1;
+    }
+    __syncthreads();
+    for (int j = tid; j < nb; j += NTHR) {
+      gfl[j] = fl[j];
+      if (sm) sm[j] = fl[j];
+    }
+    __syncthreads();
+  }
+}
+
 // One workgroup per (batch, query head): VS flags of both directions by the
 // gamma-cumsum rule (PE heads: all zero).
 __global__ __launch_bounds__(NTHR) void flex_vs_kernel(const int8_t* __restrict__ pattern,
@@ -168,27 +271,7 @@ __global__ __launch_bounds__(NTHR) void flex_vs_kernel(const int8_t* __restrict_
     for (int j = tid; j < nb; j += NTHR) fl[j] = 0;
     if (tid == 0) cut = nb;
     __syncthreads();
-    // bitonic sort into (score descending, index ascending)
-    for (int kk = 2; kk <= np; kk <<= 1) {
-      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < np; i += NTHR) {
-          const int l = i ^ jj;
-          if (l > i) {
-            const float a = sv[i], c = sv[l];
-            const int ia = si[i], ic = si[l];
-            const bool l_first = c > a || (c == a && ic < ia);   // element l belongs before element i
-            const bool up = (i & kk) == 0;
-            if (up ? l_first : !l_first) {
-              sv[i] = c;
-              sv[l] = a;
-              si[i] = ic;
-              si[l] = ia;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
+    sort_desc(sv, si, np);
     // inclusive prefix sums in fp64 over the sorted scores: the first position reaching gamma
     const int per = (np + NTHR - 1) / NTHR;
     const int lo = tid * per, hi = lo + per < nb ? lo + per : nb;
@@ -251,6 +334,13 @@ hipError_t launch_flex_route(const Dims& dm, float tau, const uint16_t* q, const
     flex_route_kernel<64><<<(unsigned)dm.bh, NTHR, 0, st>>>(q, kbar, p_vert, jsd, pattern, dm.n, dm.h_q, dm.group,
                                                            tau, scale);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_median_vs(const Dims& dm, float alpha, int kmin_blocks, const int8_t* pattern, const float* p_vert,
+                            const float* p_slash, uint8_t* vsflags, uint8_t* sel_mask, hipStream_t st) {
+  median_vs_kernel<<<(unsigned)dm.bh, NTHR, 0, st>>>(pattern, p_vert, p_slash, vsflags, sel_mask, dm.nb, alpha,
+                                                     kmin_blocks);
   return hipGetLastError();
 }
 

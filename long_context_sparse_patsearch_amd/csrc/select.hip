@@ -390,7 +390,7 @@ __global__ __launch_bounds__(NTHR) void pe_find_kernel(const int8_t* __restrict_
 __global__ __launch_bounds__(64) void row_count_kernel(const int8_t* __restrict__ pattern, const uint8_t* __restrict__ vsflags,
                                                        const float* __restrict__ abar, const u64* __restrict__ state,
                                                        int64_t* __restrict__ rowcnt, int32_t* __restrict__ eqcnt,
-                                                       int32_t* __restrict__ seltake, int nb, int64_t tri) {
+                                                       int32_t* __restrict__ seltake, int nb, int64_t tri, int band) {
   const int64_t r = blockIdx.x;
   const int64_t bh = r / nb;
   const int qb = (int)(r % nb);
@@ -401,7 +401,9 @@ __global__ __launch_bounds__(64) void row_count_kernel(const int8_t* __restrict_
     int cnt = 0;
     for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
       const int kb = kb0 + lane;
-      const bool sel = kb <= qb && (vert[kb] | slash[nb - 1 - qb + kb]);
+      // tile (qb, kb) lies on block diagonal qb - kb: selected slash block nb-1-(qb-kb), or with
+      // the band, the slash block of diagonal qb-kb-1 (nb-(qb-kb)), whose tokens reach this tile
+      const bool sel = kb <= qb && (vert[kb] | slash[nb - 1 - qb + kb] | (band && kb < qb && slash[nb - qb + kb]));
       cnt += __popcll(__ballot(sel));
     }
     if (lane == 0) { rowcnt[r] = cnt; eqcnt[r] = 0; seltake[r] = 0; }
@@ -533,7 +535,7 @@ __global__ __launch_bounds__(NTHR) void scan_apply_kernel(const int64_t* __restr
 __global__ __launch_bounds__(64) void fill_kernel(const int8_t* __restrict__ pattern, const uint8_t* __restrict__ vsflags,
                                                   const float* __restrict__ abar, const u64* __restrict__ state,
                                                   const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ seltake,
-                                                  int32_t* __restrict__ col_idx, int nb, int64_t tri) {
+                                                  int32_t* __restrict__ col_idx, int nb, int64_t tri, int band) {
   const int64_t r = blockIdx.x;
   const int64_t bh = r / nb;
   const int qb = (int)(r % nb);
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(64) void fill_kernel(const int8_t* __restrict__ pat
     const uint8_t* slash = vert + nb;
     for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
       const int kb = kb0 + lane;
-      const bool sel = kb <= qb && (vert[kb] | slash[nb - 1 - qb + kb]);
+      const bool sel = kb <= qb && (vert[kb] | slash[nb - 1 - qb + kb] | (band && kb < qb && slash[nb - qb + kb]));
       const u64 bal = __ballot(sel);
       if (sel) out[pos + __popcll(bal & below)] = kb;
       pos += __popcll(bal);
@@ -575,11 +577,15 @@ __global__ __launch_bounds__(64) void fill_kernel(const int8_t* __restrict__ pat
 template <int D>
 hipError_t select_impl(const Dims& dm, float alpha, float gamma, int kmin, const uint16_t* q, const uint16_t* k,
                        const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
-                       int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st, int vs_rule) {
+                       int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st, int vs_rule,
+                       int band) {
   const int nb = dm.nb;
   const unsigned bh = (unsigned)dm.bh;
   if (vs_rule == VS_GAMMA_CUMSUM) {
     const hipError_t e = launch_flex_vs(dm, gamma, kmin, pattern, p_vert, p_slash, ws.vsflags, sel_mask, st);
+    if (e != hipSuccess) return e;
+  } else if (vs_rule == VS_MEDIAN_FLOOR) {
+    const hipError_t e = launch_median_vs(dm, alpha, kmin, pattern, p_vert, p_slash, ws.vsflags, sel_mask, st);
     if (e != hipSuccess) return e;
   } else {
     vs_select_kernel<<<bh, NTHR, 0, st>>>(pattern, p_vert, p_slash, ws.vsflags, sel_mask, nb, alpha, kmin);
@@ -601,14 +607,14 @@ hipError_t select_impl(const Dims& dm, float alpha, float gamma, int kmin, const
     pe_find_kernel<<<bh, NTHR, 0, st>>>(pattern, ws.hist_mass, ws.hist_cnt, ws.pe_state, pass);
   }
   row_count_kernel<<<(unsigned)dm.rows, 64, 0, st>>>(pattern, ws.vsflags, ws.abar, ws.pe_state, ws.rowcnt, ws.eqcnt,
-                                                      ws.seltake, nb, dm.tri);
+                                                      ws.seltake, nb, dm.tri, band);
   pe_ties_kernel<<<bh, NTHR, 0, st>>>(pattern, ws.pe_state, ws.rowcnt, ws.eqcnt, ws.seltake, nb);
   const int64_t nblk = (dm.rows + SCAN_PER - 1) / SCAN_PER;
   scan_blocks_kernel<<<(unsigned)nblk, NTHR, 0, st>>>(ws.rowcnt, ws.scan_part, dm.rows);
   scan_top_kernel<<<1, NTHR, 0, st>>>(ws.scan_part, nblk);
   scan_apply_kernel<<<(unsigned)nblk, NTHR, 0, st>>>(ws.rowcnt, ws.scan_part, row_ptr, dm.rows, nblk);
   fill_kernel<<<(unsigned)dm.rows, 64, 0, st>>>(pattern, ws.vsflags, ws.abar, ws.pe_state, row_ptr, ws.seltake, col_idx,
-                                                nb, dm.tri);
+                                                nb, dm.tri, band);
   return hipGetLastError();
 }
 
@@ -641,12 +647,13 @@ size_t select_ws_layout(const Dims& dm, SelectWs* ws, char* base) {
 
 hipError_t launch_select(const Dims& dm, float alpha, float gamma, int kmin_blocks, const uint16_t* q, const uint16_t* k,
                          const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
-                         int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st, int vs_rule) {
+                         int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st, int vs_rule,
+                         int band) {
   if (dm.d == 128)
     return select_impl<128>(dm, alpha, gamma, kmin_blocks, q, k, pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask,
-                            ws, st, vs_rule);
+                            ws, st, vs_rule, band);
   return select_impl<64>(dm, alpha, gamma, kmin_blocks, q, k, pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask, ws,
-                         st, vs_rule);
+                         st, vs_rule, band);
 }
 
 }  // namespace crisp

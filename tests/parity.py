@@ -41,9 +41,9 @@ def device_inputs(inp):
     return tuple(to_dev(inp[t]) for t in ("q", "k", "v"))
 
 
-def gpu_layer(q, k, v, cfg, attn=True, out_dtype=torch.float32):
+def gpu_layer(q, k, v, cfg, attn=True, out_dtype=torch.float32, variant=0):
     r = crisp.route(q, k, cfg)
-    s = crisp.select(q, k, r, cfg, with_mask=True)
+    s = crisp.select(q, k, r, cfg, with_mask=True, variant=variant)
     o = crisp.sparse_attn(q, k, v, s, cfg, out_dtype=out_dtype) if attn else None
     torch.cuda.synchronize()
     row_ptr = s["row_ptr"].cpu().numpy()
@@ -100,7 +100,7 @@ def _vs_exempt(p, j, alpha, mu, cnt, kmin):
     return False
 
 
-def check_vs(g, bh, r, alpha, kmin, nb):
+def check_vs(g, bh, r, alpha, kmin, nb, band=False):
     mask = g["mask"][bh]
     sets = {}
     for dir_, key_sel, key_p, key_mu, key_cnt in ((0, "sel_v", "p_v", "mu_v", "cnt_v"), (1, "sel_s", "p_s", "mu_s", "cnt_s")):
@@ -111,7 +111,7 @@ def check_vs(g, bh, r, alpha, kmin, nb):
             assert _vs_exempt(r[key_p], j, alpha, r[key_mu], r[key_cnt], kmin), \
                 (bh, dir_, j, r[key_p][j], alpha * r[key_mu])
         sets[dir_] = np.array(sorted(gs), dtype=np.int64)
-    want = co.vs_rows(sets[0], sets[1], nb)
+    want = co.vs_rows(sets[0], sets[1], nb, band)
     got = rows_of(g, bh, nb)
     for qb in range(nb):
         assert np.array_equal(got[qb], want[qb]), (bh, qb)
@@ -140,24 +140,25 @@ def check_pe(g, bh, r, gamma, nb):
     return ndiff
 
 
-def oracle_layer(inp, cfg_kw, force_vs=None, workers=None):
-    return layer_selection(inp["q"], inp["k"], force_vs=force_vs, workers=workers, **cfg_kw)
+def oracle_layer(inp, cfg_kw, force_vs=None, workers=None, floor="mean", band=False):
+    return layer_selection(inp["q"], inp["k"], force_vs=force_vs, workers=workers, floor=floor, band=band, **cfg_kw)
 
 
-def check_selection(g, inp, ora, cfg_kw, H, nb):
+def check_selection(g, inp, ora, cfg_kw, H, nb, floor="mean", band=False):
     """Route + select checks; returns the oracle dict actually compared (after re-runs)."""
     exempt = check_route(g, ora, H, cfg_kw["tau"])
     if exempt:
         redo = {bh: v for bh, v in exempt.items() if v != ora[bh]["is_vs"]}
         if redo:
             ora = dict(ora)
-            ora.update(layer_selection(inp["q"], inp["k"], heads=list(redo), force_vs=redo, **cfg_kw))
+            ora.update(layer_selection(inp["q"], inp["k"], heads=list(redo), force_vs=redo, floor=floor,
+                                        band=band, **cfg_kw))
     kmin = cfg_kw["k_min_tokens"] // 128
     stats = dict(vs_diff=0, pe_diff=0)
     for (b, h), r in ora.items():
         bh = b * H + h
         if r["is_vs"]:
-            stats["vs_diff"] += check_vs(g, bh, r, cfg_kw["alpha"], kmin, nb)
+            stats["vs_diff"] += check_vs(g, bh, r, cfg_kw["alpha"], kmin, nb, band)
         else:
             stats["pe_diff"] += check_pe(g, bh, r, cfg_kw["gamma"], nb)
     return ora, stats

@@ -155,6 +155,18 @@ def test_flex_calls_reject_before_any_hip_call(lib):
     assert select(cap, need_s, rp=None) == NULL
 
 
+def test_select_variant_rejects_unknown_bits(lib):
+    sh, cfg = shape(), crisp.config()
+    need = crisp.workspace_bytes(sh, cfg, 1)
+    cap = crisp.max_blocks(sh)
+
+    def call(variant, cap_=cap):
+        return lib.crisp_select_variant(ctypes.byref(sh), ctypes.byref(cfg), variant, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, cap_, None, FAKE, need, None)
+    assert call(4) == PARAM and call(-1) == PARAM
+    assert call(crisp.VARIANT_MEDIAN_FLOOR | crisp.VARIANT_SLASH_BAND, cap_=cap - 1) == CAP
+
+
 def test_attention_rejects_before_any_hip_call(lib):
     sh, cfg = shape(), crisp.config()
     need = crisp.workspace_bytes(sh, cfg, 2)
