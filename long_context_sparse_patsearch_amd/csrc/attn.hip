@@ -6,18 +6,22 @@
 // sparse attention; method-steps step 4), with M_S given as a block CSR, and
 // the dense causal result the digest's FlashAttention baseline computes.
 //
-// Work item = one (head, 128-row query block); a workgroup of four waves runs
-// it, wave w holding query rows 32w..32w+31 as B operands of S^T = K Q^T.
-// Key blocks are walked in 64-key stages, double-buffered in LDS and filled by
-// direct global->LDS loads (no register staging): the K stage row-major, the
-// V stage from a V^T copy made once per call (keys contiguous per head-dim
-// row), both with an XOR swizzle of the 16-byte chunks so that every operand
-// read is bank-conflict free.  S^T and O^T += V^T P^T run on 32x32x16 bf16
-// MFMA; the online softmax stays in fp32 registers (each lane owns one query
-// column), with the 1/sqrt(d)*log2(e) scale folded into one FMA feeding exp2
-// and the output rescaled only in stages where some row maximum of the wave grows.
-// Two workgroups share a CU so that one wave's softmax runs under another
-// wave's MFMAs.  Items come from per-XCD work queues (see Queue).
+// Work item = one (head, 128-row query block).  Key blocks are walked in
+// 64-key stages, double-buffered in LDS and filled by direct global->LDS loads
+// (no register staging): the K stage row-major, the V stage from a V^T copy
+// made once per call (keys contiguous per head-dim row), both with an XOR
+// swizzle of the 16-byte chunks so that every operand read is bank-conflict
+// free.  S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA; the online
+// softmax stays in fp32 registers (each lane owns one query column), with the
+// 1/sqrt(d)*log2(e) scale folded into one FMA feeding exp2 and the output
+// rescaled only in stages where some row maximum grows.  Items come from
+// per-XCD work queues (see Queue).
+//
+// Two kernels share this frame.  d = 128 (attn_q64_kernel): two waves per
+// workgroup, 64 query rows per wave, one wave per SIMD, so that each operand
+// read from LDS feeds two MFMAs.  d = 64 (attn_kernel): four waves of 32 rows,
+// two workgroups per CU, so that one wave's softmax runs under another wave's
+// MFMAs.
 #include <math.h>
 
 #include "crisp_device.hpp"
@@ -462,6 +466,466 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// d = 128: 64 query rows per wave (two 32-row tiles), one wave per SIMD.
+//
+// Every K and V^T operand read from LDS feeds the MFMAs of both tiles, which
+// halves the operand reads per flop.  Register classes are fixed by hand:
+// the S^T accumulators (read by the softmax) in VGPRs, the O^T accumulators
+// and the Q operands (touched only by MFMAs) in AGPRs, so the MFMAs are
+// issued as inline asm and the schedule is written out in regions fenced
+// with sched_barrier: each region holds a slice of the softmax VALU work, at
+// most one operand read, and one MFMA.  The softmax of a stage is split
+// between the QK phase (weight pairs [0, Q64_P1) of each tile) and the PV
+// phase (the rest, done by the time the PV MFMAs need them, then the next
+// stage's row maxima).
+//
+// The compiler does not see the MFMAs inside the asm, so the wait states the
+// hardware needs around them are kept by construction: a weight pair is
+// written at least two regions before the PV MFMA that reads it (VALU write
+// -> MFMA read needs 2), the scores are read by VALU code only in later
+// regions or after an explicit s_nop (MFMA write -> VALU read needs 12), and
+// the output rescale ends with an s_nop (AGPR write -> MFMA read needs 2).
+// ---------------------------------------------------------------------------
+constexpr int Q64_THR = 128;       // two waves: one 128-row query block per workgroup
+constexpr int Q64_WG_PER_CU = 2;   // four waves per CU, one per SIMD
+constexpr int Q64_P1 = 10;         // weight pairs per tile computed in the QK phase (of 16)
+constexpr int Q64_AHEAD = 4;       // operand reads in flight ahead of the MFMAs
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 lds16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+// s = K Q^T tile product, s in VGPRs, q in AGPRs
+__device__ __forceinline__ void mfma_s0(f32x16& s, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16& s, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(b));
+}
+// o += V^T P^T tile product, o in AGPRs
+__device__ __forceinline__ void mfma_o(f32x16& o, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
+}
+// 13 wait states: covers an MFMA result read by VALU code (or its accumulator
+// overwritten by VALU code) right after the MFMA
+__device__ __forceinline__ void mfma_drain() {
+  fence();
+  asm volatile("s_nop 7\n\ts_nop 4" ::: "memory");
+  fence();
+}
+
+// max / sum over lanes l and l ^ 32
+__device__ __forceinline__ float halves_max(float t) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float t) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Softmax state of one stage for both tiles.  Weight pair p of tile t covers
+// accumulator registers 2p, 2p+1 (ks = p / 8) and becomes 32-bit word p % 4 of
+// the PV operand pw[t][p / 4]; its seven VALU ops are numbered k = 0..6: two
+// FMAs, two exp2, the bf16 pack, and two adds of the fp32 weights into the row
+// sum (plain adds: a v_dot2 here would wait for the MFMA in flight).
+struct Q64Soft {
+  float a0[2][16], a1[2][16];
+  u32x4 pw[2][4];
+};
+
+__device__ __forceinline__ void q64_pair_op(Q64Soft& sm, const f32x16 (&sc)[2][2], int t, int p, int k, float c2,
+                                            const float (&nm)[2], float (&l)[2]) {
+  const int ks = p >> 3, r = (2 * p) & 15;
+  switch (k) {
+    case 0: sm.a0[t][p] = fmaf(sc[t][ks][r], c2, nm[t]); break;
+    case 1: sm.a1[t][p] = fmaf(sc[t][ks][r + 1], c2, nm[t]); break;
+    case 2: sm.a0[t][p] = fast_exp2(sm.a0[t][p]); break;
+    case 3: sm.a1[t][p] = fast_exp2(sm.a1[t][p]); break;
+    case 4: sm.pw[t][p >> 2][p & 3] = pack_bf16x2(sm.a0[t][p], sm.a1[t][p]); break;
+    case 5: l[t] += sm.a0[t][p]; break;
+    default: l[t] += sm.a1[t][p];
+  }
+}
+// op q of the pair program over pairs [p0, p0 + np) of both tiles (pair-major, tiles alternating)
+__device__ __forceinline__ void q64_pair_prog(Q64Soft& sm, const f32x16 (&sc)[2][2], int p0, int q, float c2,
+                                              const float (&nm)[2], float (&l)[2]) {
+  const int pp = q / 7, k = q % 7;
+  q64_pair_op(sm, sc, pp & 1, p0 + (pp >> 1), k, c2, nm, l);
+}
+
+// QK phase.  Regions i = 0..31: MFMA i is S_n[t][ks] += K[ks][st] Q[t][st]^T
+// with i = 2 (8 ks + st) + t; operand read r = 8 ks + st feeds MFMAs 2r, 2r+1.
+// The read stream continues into the PV phase: reads 16..19 are its first V^T
+// operands (the V^T stage is already resident).
+template <bool HAS_NEXT>
+__device__ __forceinline__ void q64_qk(const char* kbase, const char* vbase, const uint32_t (&koff)[8],
+                                       const uint32_t (&voff)[4], const u32x4 (&qf)[2][8], f32x16 (&sn)[2][2],
+                                       const f32x16 (&sc)[2][2], float c2, const float (&nm)[2], Q64Soft& sm,
+                                       float (&l)[2], u32x4 (&op)[Q64_AHEAD + 1]) {
+  constexpr int KROW = 256, VROW = KS * 2;
+  constexpr int NOPS = Q64_P1 * 2 * 7;
+  auto read = [&](int r) -> u32x4 {
+    if (r < 16) return lds16(kbase + koff[r & 7] + 32 * (r >> 3) * KROW);
+    const int v = r - 16;
+    return lds16(vbase + voff[v >> 2] + 32 * (v & 3) * VROW);
+  };
+#pragma unroll
+  for (int r = 0; r < Q64_AHEAD; ++r) op[r % (Q64_AHEAD + 1)] = read(r);
+  fence();
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+#pragma unroll
+    for (int q = (i * NOPS) / 32; q < ((i + 1) * NOPS) / 32; ++q) q64_pair_prog(sm, sc, 0, q, c2, nm, l);
+    const int r = i >> 1;
+    if (!(i & 1)) op[(r + Q64_AHEAD) % (Q64_AHEAD + 1)] = read(r + Q64_AHEAD);
+    if (HAS_NEXT) {
+      const int t = i & 1, ks = r >> 3, st = r & 7;
+      if (st == 0) mfma_s0(sn[t][ks], op[r % (Q64_AHEAD + 1)], qf[t][st]);
+      else mfma_s(sn[t][ks], op[r % (Q64_AHEAD + 1)], qf[t][st]);
+    }
+    fence();
+  }
+  // keep the weights computed here in this phase
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    asm volatile("" ::"v"(sm.pw[t][0]), "v"(sm.pw[t][1]), "v"(sm.pw[t][2][0]), "v"(sm.pw[t][2][1]), "v"(l[t]));
+}
+
+// PV phase.  Regions i = 0..31: MFMA i is O[t][ds] += V^T[cc][ds] P[t][cc]
+// with i = 2 (4 cc + ds) + t; V^T read r = 4 cc + ds (stream index 16 + r).
+// Pair ops [Q64_P1, 16) run in regions 0..21 (the last weight is written two
+// regions before the first cc = 3 MFMA), the row maxima of S_n in 22..31.
+template <bool HAS_NEXT>
+__device__ __forceinline__ void q64_pv(const char* vbase, const uint32_t (&voff)[4], f32x16 (&o)[2][4],
+                                       const f32x16 (&sc)[2][2], float c2, const float (&nm)[2], Q64Soft& sm,
+                                       float (&l)[2], const f32x16 (&sn)[2][2], float (&tmax)[2],
+                                       u32x4 (&op)[Q64_AHEAD + 1]) {
+  constexpr int VROW = KS * 2;
+  constexpr int NOPS = (16 - Q64_P1) * 2 * 7;
+  constexpr int NMAX = 2 * 17;
+  float xm[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (i < 22) {
+#pragma unroll
+      for (int q = (i * NOPS) / 22; q < ((i + 1) * NOPS) / 22; ++q) q64_pair_prog(sm, sc, Q64_P1, q, c2, nm, l);
+    } else if (HAS_NEXT) {
+      const int j = i - 22;
+#pragma unroll
+      for (int q = (j * NMAX) / 10; q < ((j + 1) * NMAX) / 10; ++q) {
+        const int t = q / 17, mq = q % 17;
+        if (mq < 16) {
+          const int ks = mq >> 3, r = (2 * mq) & 15;
+          xm[t] = fmaxf(fmaxf(xm[t], sn[t][ks][r]), sn[t][ks][r + 1]);
+        } else {
+          tmax[t] = halves_max(xm[t]);
+        }
+      }
+    }
+    const int r = i >> 1;
+    if (!(i & 1) && r + Q64_AHEAD < 16) {
+      const int v = r + Q64_AHEAD;
+      op[(16 + v) % (Q64_AHEAD + 1)] = lds16(vbase + voff[v >> 2] + 32 * (v & 3) * VROW);
+    }
+    const int t = i & 1, cc = r >> 2, ds = r & 3;
+    mfma_o(o[t][ds], op[(16 + r) % (Q64_AHEAD + 1)], sm.pw[t][cc]);
+    fence();
+  }
+}
+
+__device__ __forceinline__ void q64_update(const float (&tmax)[2], float c2, float (&m)[2], float (&corr)[2],
+                                           bool (&any)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float tmu = tmax[t] * c2;
+    const bool need = tmu > m[t] + RESCALE_LOG2;
+    any[t] = __ballot(need) != 0;
+    const float mn = need ? tmu : m[t];
+    corr[t] = fast_exp2(m[t] - mn);
+    m[t] = mn;
+  }
+}
+
+// O *= corr for the tiles whose row maximum grew.  Written as asm (AGPR read,
+// multiply, AGPR write per register) so that no compiler-generated code
+// touches the AGPR accumulators inside the stage loop; the trailing s_nop
+// covers the AGPR write -> MFMA accumulator read of the next PV MFMA.
+__device__ __forceinline__ void agpr_scale(f32x16& o, float c) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float e = o[r], tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(e), "=&v"(tmp)
+                 : "v"(c));
+    o[r] = e;
+  }
+}
+__device__ __forceinline__ void q64_rescale(f32x16 (&o)[2][4], const float (&corr)[2], const bool (&any)[2]) {
+  fence();
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    if (any[t]) {
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) agpr_scale(o[t][ds], corr[t]);
+      asm volatile("s_nop 2" ::: "memory");
+      fence();
+    }
+}
+
+__device__ __forceinline__ void q64_mask(f32x16 (&s)[2][2], int kloc0, int qloc0, int lane) {
+  mfma_drain();
+  mask_diag(s[0], kloc0, qloc0, lane);
+  mask_diag(s[1], kloc0, qloc0 + 32, lane);
+  fence();
+}
+
+template <bool DENSE, bool OUT_BF16>
+__global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_q64_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
+    const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_cap,
+    void* __restrict__ out, int n, int h_q, int group, Queue qd, int* __restrict__ counters, float c2) {
+  constexpr int D = 128;
+  using S = Stage<D>;
+  // LDS: K stage buffers 0 and 1, then V^T stage buffers 0 and 1 (as in attn_kernel)
+  __shared__ __align__(16) char lds[2 * S::KBYTES + 2 * S::VBYTES];
+  __shared__ int item;
+  const int x = (int)(blockIdx.x % NXCD);
+  const int w = wave_id(), lane = lane_id();
+  const int hi = lane >> 5;
+  const int nb = n / BLK;
+  const int h_kv = h_q / group;
+
+  uint32_t koff[S::NSTEP], voff[4];
+  {
+    const int krow = key_row_of_lane(lane & 31);
+    const int kfix = krow & 15;
+    const int vrow = lane & 31;
+    const int vfix = (vrow >> 1) & 7;
+#pragma unroll
+    for (int st = 0; st < S::NSTEP; ++st) koff[st] = krow * S::KROW + (((2 * st + hi) ^ kfix) * 16);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) voff[cc] = vrow * S::VROW + (((2 * cc + hi) ^ vfix) * 16);
+  }
+  const char* kbuf0 = lds;
+  const char* kbuf1 = lds + S::KBYTES;
+  const char* vbuf0 = lds + 2 * S::KBYTES;
+  const char* vbuf1 = vbuf0 + S::VBYTES;
+  // Direct loads: load i (0..7) of wave w fills LDS chunks (2i + w)*64 + lane of
+  // a stage buffer.  K: row 8i + 4w + lane/16, whose swizzle alternates with
+  // the parity of i (even loads use kd0, odd ones kd1, each pair 16 rows =
+  // 4 KiB further).  V^T: row 16i + 8w + lane/8, one swizzle for all i.
+  uint32_t kd0, kd1, vd0;
+  {
+    const int pc = lane & 15;
+    const int r0 = 4 * w + (lane >> 4), r1 = r0 + 8;
+    kd0 = (uint32_t)(r0 * D + (pc ^ (r0 & 15)) * 8) * 2u;
+    kd1 = (uint32_t)(r1 * D + (pc ^ (r1 & 15)) * 8) * 2u;
+    const int vr0 = 8 * w + (lane >> 3);
+    vd0 = (uint32_t)(vr0 * n + ((lane & 7) ^ ((vr0 >> 1) & 7)) * 8) * 2u;
+  }
+  const size_t vstep = (size_t)16 * n * 2;   // 16 V^T rows
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)lds);
+  const uint32_t lds0w = lds0 + (uint32_t)w * 1024u;
+
+  for (;;) {
+    if (threadIdx.x == 0) item = atomicAdd(&counters[x], 1);
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(item);
+    __syncthreads();
+    if (u >= qd.per_queue) break;
+    int qb;
+    int64_t bh;
+    if (!queue_item(qd, x, u, qb, bh)) continue;
+
+    const int b = (int)(bh / h_q), h = (int)(bh % h_q), g = h / group;
+    const char* kgb = reinterpret_cast<const char*>(k + ((size_t)b * h_kv + g) * n * D);
+    const char* vgb = reinterpret_cast<const char*>(vt + ((size_t)b * h_kv + g) * (size_t)D * n);
+    auto issue_k = [&](int kb, int hf, uint32_t lbuf) {
+      const char* gb = kgb + (size_t)(kb * BLK + hf * KS) * D * 2;
+      const uint32_t lb = lds0w + lbuf;
+      dma16s<0>(kd0, gb, lb);
+      dma16s<2048>(kd1, gb, lb);
+      dma16s<4096>(kd0, gb + 4096, lb);
+      dma16s<6144>(kd1, gb + 4096, lb);
+      dma16s<8192>(kd0, gb + 8192, lb);
+      dma16s<10240>(kd1, gb + 8192, lb);
+      dma16s<12288>(kd0, gb + 12288, lb);
+      dma16s<14336>(kd1, gb + 12288, lb);
+    };
+    auto issue_v = [&](int kb, int hf, uint32_t lbuf) {
+      const char* gb = vgb + (size_t)(kb * BLK + hf * KS) * 2;
+      const uint32_t lb = lds0w + lbuf;
+      dma16s<0>(vd0, gb, lb);
+      dma16s<2048>(vd0, gb + vstep, lb);
+      dma16s<4096>(vd0, gb + 2 * vstep, lb);
+      dma16s<6144>(vd0, gb + 3 * vstep, lb);
+      dma16s<8192>(vd0, gb + 4 * vstep, lb);
+      dma16s<10240>(vd0, gb + 5 * vstep, lb);
+      dma16s<12288>(vd0, gb + 6 * vstep, lb);
+      dma16s<14336>(vd0, gb + 7 * vstep, lb);
+    };
+    constexpr uint32_t LK0 = 0, LK1 = S::KBYTES, LV0 = 2 * S::KBYTES, LV1 = 2 * S::KBYTES + S::VBYTES;
+
+    int64_t t0, t1;
+    if (DENSE) {
+      t0 = 0;
+      t1 = qb + 1;
+    } else {
+      const int64_t r = bh * nb + qb;
+      t0 = row_ptr[r];
+      t1 = row_ptr[r + 1];
+      t0 = t0 < 0 ? 0 : (t0 > col_cap ? col_cap : t0);
+      t1 = t1 < t0 ? t0 : (t1 > col_cap ? col_cap : t1);
+    }
+    int64_t cb = -1;
+    int cval = -1;
+    uint64_t cmask = 0;
+    auto next_valid = [&](int64_t p) -> int64_t {
+      if (DENSE) return p;
+      for (;;) {
+        if (p >= t1) return t1;
+        if (cb < 0 || p >= cb + 64) {
+          cb = p;
+          cval = (p + lane < t1) ? col_idx[p + lane] : -1;
+          cmask = __ballot(cval >= 0 && cval <= qb);
+        }
+        const uint64_t bits = cmask >> (int)(p - cb);
+        if (bits) return p + __builtin_ctzll(bits);
+        p = cb + 64;
+      }
+    };
+    auto entry = [&](int64_t p) -> int {
+      if (DENSE) return (int)p;
+      return __builtin_amdgcn_readlane(cval, (int)(p - cb));
+    };
+
+    const int qloc0 = 64 * w + (lane & 31);   // query row (in the block) of tile 0; tile 1 is 32 further
+    u32x4 qf[2][S::NSTEP];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* qp = q + ((size_t)bh * n + (size_t)qb * BLK + qloc0 + 32 * t) * D + 8 * hi;
+#pragma unroll
+      for (int s = 0; s < S::NSTEP; ++s) qf[t][s] = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+    }
+    f32x16 o[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[t][i] = f32x16{};
+    float m[2] = {M_INIT, M_INIT}, l[2] = {0.f, 0.f}, corr[2] = {1.f, 1.f};
+    bool any[2] = {false, false};
+
+    int64_t pc = next_valid(t0);
+    if (pc < t1) {
+      int kb = entry(pc);
+      int64_t pn = next_valid(pc + 1);
+      int kbn = pn < t1 ? entry(pn) : -1;
+      f32x16 sa[2][2], sb[2][2];
+      Q64Soft sm;
+      u32x4 op[Q64_AHEAD + 1];
+      float tm[2];
+      issue_k(kb, 0, LK0);
+      vm_wait();
+      __syncthreads();
+      issue_k(kb, 1, LK1);
+      issue_v(kb, 0, LV0);
+      fence();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const u32x4 kop = lds16(kbuf0 + koff[r & 7] + 32 * (r >> 3) * S::KROW);
+        if ((r & 7) == 0) {
+          mfma_s0(sa[0][r >> 3], kop, qf[0][r & 7]);
+          mfma_s0(sa[1][r >> 3], kop, qf[1][r & 7]);
+        } else {
+          mfma_s(sa[0][r >> 3], kop, qf[0][r & 7]);
+          mfma_s(sa[1][r >> 3], kop, qf[1][r & 7]);
+        }
+      }
+      mfma_drain();
+      if (kb == qb) {
+        mask_diag(sa[0], 0, qloc0, lane);
+        mask_diag(sa[1], 0, qloc0 + 32, lane);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float xm = -INFINITY;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xm = fmaxf(xm, sa[t][ks][r]);
+        tm[t] = halves_max(xm);
+      }
+      q64_update(tm, c2, m, corr, any);
+      for (;;) {
+        // step A: current = (kb, 0) in sa, next = (kb, 1) -> sb
+        vm_wait();
+        __syncthreads();
+        if (kbn >= 0) issue_k(kbn, 0, LK0);
+        issue_v(kb, 1, LV1);
+        l[0] *= corr[0];
+        l[1] *= corr[1];
+        {
+          const float nm[2] = {-m[0], -m[1]};
+          q64_qk<true>(kbuf1, vbuf0, koff, voff, qf, sb, sa, c2, nm, sm, l, op);
+          q64_rescale(o, corr, any);
+          if (kb == qb) q64_mask(sb, KS, qloc0, lane);
+          q64_pv<true>(vbuf0, voff, o, sa, c2, nm, sm, l, sb, tm, op);
+        }
+        q64_update(tm, c2, m, corr, any);
+
+        // step B: current = (kb, 1) in sb, next = (kbn, 0) -> sa
+        vm_wait();
+        __syncthreads();
+        l[0] *= corr[0];
+        l[1] *= corr[1];
+        if (kbn >= 0) {
+          issue_k(kbn, 1, LK1);
+          issue_v(kbn, 0, LV0);
+        }
+        {
+          const float nm[2] = {-m[0], -m[1]};
+          q64_qk<true>(kbuf0, vbuf1, koff, voff, qf, sa, sb, c2, nm, sm, l, op);
+          q64_rescale(o, corr, any);
+          if (kbn == qb) q64_mask(sa, 0, qloc0, lane);
+          q64_pv<true>(vbuf1, voff, o, sb, c2, nm, sm, l, sa, tm, op);
+        }
+        if (kbn < 0) break;
+        q64_update(tm, c2, m, corr, any);
+        kb = kbn;
+        pc = pn;
+        pn = next_valid(pc + 1);
+        kbn = pn < t1 ? entry(pn) : -1;
+      }
+      mfma_drain();
+    }
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float lt = halves_sum(l[t]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const size_t orow = (size_t)bh * n + (size_t)qb * BLK + qloc0 + 32 * t;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int d = 32 * ds + 8 * grp + 4 * hi;
+          const float a0 = o[t][ds][4 * grp] * inv, a1 = o[t][ds][4 * grp + 1] * inv;
+          const float a2 = o[t][ds][4 * grp + 2] * inv, a3 = o[t][ds][4 * grp + 3] * inv;
+          if (OUT_BF16) {
+            uint2 uu;
+            uu.x = pack_bf16x2(a0, a1);
+            uu.y = pack_bf16x2(a2, a3);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + orow * D + d) = uu;
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + orow * D + d) = make_float4(a0, a1, a2, a3);
+          }
+        }
+    }
+  }
+}
+
 // V [bg][n][D] -> V^T [bg][D][n], 64-key tiles through LDS.
 template <int D>
 __global__ __launch_bounds__(NTHR) void transpose_v_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
@@ -527,6 +991,17 @@ hipError_t attn_launch(const Dims& dm, const uint16_t* q, const uint16_t* k, con
   const unsigned grid = (unsigned)(items < slots ? items : slots);
   zero_counters_kernel<<<1, 64, 0, st>>>(counters);
   transpose_v_kernel<D><<<dim3(dm.n / KS, (unsigned)(dm.batch * dm.h_kv)), NTHR, 0, st>>>(v, vt, dm.n);
+  if constexpr (D == 128) {
+    const int64_t slots64 = (int64_t)(cu_count() * Q64_WG_PER_CU + NXCD - 1) / NXCD * NXCD;
+    const unsigned grid64 = (unsigned)(items < slots64 ? items : slots64);
+    if (out_bf16)
+      attn_q64_kernel<DENSE, true><<<grid64, Q64_THR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
+                                                               dm.group, qd, counters, c2);
+    else
+      attn_q64_kernel<DENSE, false><<<grid64, Q64_THR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
+                                                                dm.group, qd, counters, c2);
+    return hipGetLastError();
+  }
   if (out_bf16)
     attn_kernel<D, DENSE, true><<<grid, NTHR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
                                                        dm.group, qd, counters, c2);
