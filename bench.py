@@ -474,7 +474,7 @@ def main():
         "dense_ms": None if dense_ms is None else round(dense_ms, 2),
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / res["ms_per_layer"], 3),
         "dense_mfma_util": None if dense_tf is None else round(dense_tf / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel (crisp_sparse_attn)",
+        "roofline": {"bound": "mfma", "kernel": "attn_q64_kernel (crisp_sparse_attn)",
                      "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flop_per_launch": res["attn_flop"], "avg_launch_ms": res["stage_ms"]["attn"]},

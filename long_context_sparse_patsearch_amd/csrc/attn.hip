@@ -714,18 +714,23 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const char* vbuf1 = vbuf0 + S::VBYTES;
   // Direct loads: load i (0..7) of wave w fills LDS chunks (2i + w)*64 + lane of
   // a stage buffer.  K: row 8i + 4w + lane/16, whose swizzle alternates with
-  // the parity of i (even loads use kd0, odd ones kd1, each pair 16 rows =
-  // 4 KiB further).  V^T: row 16i + 8w + lane/8, one swizzle for all i.
-  uint32_t kd0, kd1, vd0;
+  // the parity of i.  V^T: row 16i + 8w + lane/8, one swizzle for all i.  The
+  // eight per-lane byte offsets of each are kept in registers, so that all
+  // loads of a stage share one scalar base address.
+  uint32_t kd[8], vd[8];
   {
     const int pc = lane & 15;
     const int r0 = 4 * w + (lane >> 4), r1 = r0 + 8;
-    kd0 = (uint32_t)(r0 * D + (pc ^ (r0 & 15)) * 8) * 2u;
-    kd1 = (uint32_t)(r1 * D + (pc ^ (r1 & 15)) * 8) * 2u;
+    const uint32_t kd0 = (uint32_t)(r0 * D + (pc ^ (r0 & 15)) * 8) * 2u;
+    const uint32_t kd1 = (uint32_t)(r1 * D + (pc ^ (r1 & 15)) * 8) * 2u;
     const int vr0 = 8 * w + (lane >> 3);
-    vd0 = (uint32_t)(vr0 * n + ((lane & 7) ^ ((vr0 >> 1) & 7)) * 8) * 2u;
+    const uint32_t vd0 = (uint32_t)(vr0 * n + ((lane & 7) ^ ((vr0 >> 1) & 7)) * 8) * 2u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      kd[i] = ((i & 1) ? kd1 : kd0) + (uint32_t)(i >> 1) * 4096u;
+      vd[i] = vd0 + (uint32_t)i * 16u * (uint32_t)n * 2u;   // 16 V^T rows per load
+    }
   }
-  const size_t vstep = (size_t)16 * n * 2;   // 16 V^T rows
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)lds);
   const uint32_t lds0w = lds0 + (uint32_t)w * 1024u;
 
@@ -745,26 +750,26 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
     auto issue_k = [&](int kb, int hf, uint32_t lbuf) {
       const char* gb = kgb + (size_t)(kb * BLK + hf * KS) * D * 2;
       const uint32_t lb = lds0w + lbuf;
-      dma16s<0>(kd0, gb, lb);
-      dma16s<2048>(kd1, gb, lb);
-      dma16s<4096>(kd0, gb + 4096, lb);
-      dma16s<6144>(kd1, gb + 4096, lb);
-      dma16s<8192>(kd0, gb + 8192, lb);
-      dma16s<10240>(kd1, gb + 8192, lb);
-      dma16s<12288>(kd0, gb + 12288, lb);
-      dma16s<14336>(kd1, gb + 12288, lb);
+      dma16s<0>(kd[0], gb, lb);
+      dma16s<2048>(kd[1], gb, lb);
+      dma16s<4096>(kd[2], gb, lb);
+      dma16s<6144>(kd[3], gb, lb);
+      dma16s<8192>(kd[4], gb, lb);
+      dma16s<10240>(kd[5], gb, lb);
+      dma16s<12288>(kd[6], gb, lb);
+      dma16s<14336>(kd[7], gb, lb);
     };
     auto issue_v = [&](int kb, int hf, uint32_t lbuf) {
       const char* gb = vgb + (size_t)(kb * BLK + hf * KS) * 2;
       const uint32_t lb = lds0w + lbuf;
-      dma16s<0>(vd0, gb, lb);
-      dma16s<2048>(vd0, gb + vstep, lb);
-      dma16s<4096>(vd0, gb + 2 * vstep, lb);
-      dma16s<6144>(vd0, gb + 3 * vstep, lb);
-      dma16s<8192>(vd0, gb + 4 * vstep, lb);
-      dma16s<10240>(vd0, gb + 5 * vstep, lb);
-      dma16s<12288>(vd0, gb + 6 * vstep, lb);
-      dma16s<14336>(vd0, gb + 7 * vstep, lb);
+      dma16s<0>(vd[0], gb, lb);
+      dma16s<2048>(vd[1], gb, lb);
+      dma16s<4096>(vd[2], gb, lb);
+      dma16s<6144>(vd[3], gb, lb);
+      dma16s<8192>(vd[4], gb, lb);
+      dma16s<10240>(vd[5], gb, lb);
+      dma16s<12288>(vd[6], gb, lb);
+      dma16s<14336>(vd[7], gb, lb);
     };
     constexpr uint32_t LK0 = 0, LK1 = S::KBYTES, LV0 = 2 * S::KBYTES, LV1 = 2 * S::KBYTES + S::VBYTES;
 
