@@ -63,6 +63,10 @@ R19 FlexPrefill's VS index is Algorithm 3 with the per-direction noise-floor
     rule replaced by the gamma-cumsum budget rule (same gamma as the PE path):
     the shortest descending prefix of p_d reaching gamma, its count clipped to
     [k_min, N_b] (top-k), then the anchors {0, N_b-1}.
+R22 Per-row PE (variant of R11): the gamma-cumsum runs inside each row of the
+    pooled map, which is a distribution over kb <= qb: a row keeps its own
+    shortest descending prefix reaching gamma (ties to the lower block, R10;
+    the whole row if it falls short, R15), and its diagonal as in R13.
 """
 from __future__ import annotations
 
@@ -221,18 +225,33 @@ def gamma_cumsum(x: np.ndarray, gamma: float):
     return order[:k], order, cs
 
 
-def pe_select(a_bar: np.ndarray, gamma: float):
+def pe_select(a_bar: np.ndarray, gamma: float, per_row: bool = False):
     """Global gamma-cumsum over the flattened block-causal map (R11, R13).
 
     Entries are the valid (qb, kb <= qb) cells in row-major order, scored
     x = A_bar / N_b.  Returns dict(rows, x, qb, kb, order, cs, kept) where
-    ``kept`` are positions into x (the flattened valid cells).
+    ``kept`` are positions into x (the flattened valid cells).  With
+    ``per_row`` each row runs its own gamma-cumsum over A_bar[qb, :qb+1]
+    (R22); the dict then holds, per row, ``row_order`` and ``row_cs`` (the
+    row's descending order and prefix sums) and ``row_kept``.
     """
     nb = a_bar.shape[0]
     qb, kb = np.tril_indices(nb)
     x = a_bar[qb, kb] / nb
-    kept, order, cs = gamma_cumsum(x, gamma)
     mask = np.zeros((nb, nb), dtype=bool)
+    if per_row:
+        row_kept, row_order, row_cs = [], [], []
+        for r in range(nb):
+            k_r, o_r, c_r = gamma_cumsum(a_bar[r, : r + 1], gamma)
+            mask[r, k_r] = True
+            row_kept.append(k_r)
+            row_order.append(o_r)
+            row_cs.append(c_r)
+        mask[np.diag_indices(nb)] = True
+        rows = [np.nonzero(mask[r, : r + 1])[0].astype(np.int64) for r in range(nb)]
+        return dict(rows=rows, x=x, qb=qb, kb=kb, per_row=True, row_kept=row_kept, row_order=row_order,
+                    row_cs=row_cs)
+    kept, order, cs = gamma_cumsum(x, gamma)
     mask[qb[kept], kb[kept]] = True
     mask[np.arange(nb), np.arange(nb)] = True
     rows = [np.nonzero(mask[r, : r + 1])[0].astype(np.int64) for r in range(nb)]
@@ -296,13 +315,13 @@ def dense_attention(q_h, k_g, v_g, q_blocks=None, block: int = BLOCK, q_rows=Non
 # Algorithm 1: one head end to end
 # ----------------------------------------------------------------------------
 def crisp_head(q_h, k_g, *, tau=0.2, alpha=1.0, gamma=0.95, k_min_tokens=1024,
-               block=BLOCK, force_vs=None, floor="mean", band=False):
+               block=BLOCK, force_vs=None, floor="mean", band=False, pe_per_row=False):
     """Routing and selection of one query head, as Algorithm 1 assembles them.
 
     PatSearch, then VSIndex if the head routes VS, else PEIndex.  ``force_vs``
     overrides the routing decision (used to re-run a head whose structural mass
-    sits on the threshold); ``floor`` and ``band`` select the variants R20 and
-    R21.  Returns a dict with the route, the scores and the per-query-block
+    sits on the threshold); ``floor``, ``band`` and ``pe_per_row`` select the
+    variants R20, R21 and R22.  Returns a dict with the route, the scores and the per-query-block
     key-block rows.
     """
     n = q_h.shape[0]
@@ -320,7 +339,7 @@ def crisp_head(q_h, k_g, *, tau=0.2, alpha=1.0, gamma=0.95, k_min_tokens=1024,
         res.update(sel_v=sv, sel_s=ss, mu_v=mu_v, mu_s=mu_s, cnt_v=cnt_v, cnt_s=cnt_s,
                    rows=vs_rows(sv, ss, nb, band))
     else:
-        pe = pe_select(pooled_map(q_h, k_g, block), gamma)
+        pe = pe_select(pooled_map(q_h, k_g, block), gamma, per_row=pe_per_row)
         res.update(pe=pe, rows=pe["rows"])
     return res
 

@@ -34,7 +34,7 @@ def default_workers(cap: int = 16) -> int:
 
 
 def layer_selection(q_bits, k_bits, *, tau=0.2, alpha=1.0, gamma=0.95, k_min_tokens=1024,
-                    heads=None, force_vs=None, workers=None, floor="mean", band=False):
+                    heads=None, force_vs=None, workers=None, floor="mean", band=False, pe_per_row=False):
     """Routing and selection of every (batch, head) pair of one layer.
 
     ``q_bits`` [batch][h_q][n][d], ``k_bits`` [batch][h_kv][n][d] (bf16 bits).
@@ -51,7 +51,7 @@ def layer_selection(q_bits, k_bits, *, tau=0.2, alpha=1.0, gamma=0.95, k_min_tok
         q = co.bf16_to_f64(q_bits[b, h])
         k = co.bf16_to_f64(k_bits[b, h // G])
         return bh, co.crisp_head(q, k, tau=tau, alpha=alpha, gamma=gamma, k_min_tokens=k_min_tokens,
-                                 force_vs=force_vs.get(bh), floor=floor, band=band)
+                                 force_vs=force_vs.get(bh), floor=floor, band=band, pe_per_row=pe_per_row)
 
     workers = workers or default_workers()
     with _blas_limit(1):

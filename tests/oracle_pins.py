@@ -450,3 +450,50 @@ def check_slash_band_tokens(co):
         assert rows[qb].tolist() == np.nonzero(tiles[qb])[0].tolist(), qb
     plain = co.vs_rows(np.array([], dtype=np.int64), sel_s, nb)
     assert all(set(a.tolist()) <= set(b.tolist()) for a, b in zip(plain, rows))
+
+
+def check_pe_per_row_uniform_closed_form(co):
+    """Per-row PE (R22) on zero queries: row r of A_bar is uniform 1/(r+1), so the
+    row keeps its first ceil(gamma (r+1)) blocks (ties to the lower block) and
+    its diagonal."""
+    rng = np.random.default_rng(6)
+    for nb, gamma in ((24, 0.9437), (17, 0.5213)):
+        # gamma (r + 1) stays clear of integers, so rounding in the prefix sums cannot move the cut
+        assert min(abs(gamma * (r + 1) - round(gamma * (r + 1))) for r in range(nb)) > 1e-3
+        n, d = nb * B, 64
+        a_bar = co.pooled_map(np.zeros((n, d)), _rand(rng, n, d), B)
+        pe = co.pe_select(a_bar, gamma, per_row=True)
+        for r in range(nb):
+            k = int(math.ceil(gamma * (r + 1)))
+            assert pe["rows"][r].tolist() == sorted(set(range(k)) | {r}), (nb, r)
+
+
+def check_pe_per_row_brute_force(co, seed=31):
+    """Per-row PE (R22) against exhaustive search on short rows: the kept set of
+    a row is a smallest subset whose mass reaches gamma, made of the largest
+    scores (ties to the lower block), plus the diagonal."""
+    import itertools
+    rng = np.random.default_rng(seed)
+    nb = 7
+    for trial in range(6):
+        logits = rng.normal(scale=1.5, size=(nb, nb))
+        if trial == 5:
+            logits = np.round(logits)                      # force ties
+        logits[np.triu_indices(nb, 1)] = -np.inf
+        a_bar = np.exp(logits - logits.max(axis=1, keepdims=True))
+        a_bar /= a_bar.sum(axis=1, keepdims=True)
+        gamma = 0.6 + 0.05 * trial
+        pe = co.pe_select(a_bar, gamma, per_row=True)
+        for r in range(nb):
+            row = a_bar[r, : r + 1]
+            best = None
+            for size in range(1, r + 2):
+                for sub in itertools.combinations(range(r + 1), size):
+                    if row[list(sub)].sum() >= gamma:
+                        best = size
+                        break
+                if best:
+                    break
+            order = sorted(range(r + 1), key=lambda j: (-row[j], j))
+            want = set(order[:best]) | {r}
+            assert set(pe["rows"][r].tolist()) == want, (trial, r)

@@ -44,6 +44,11 @@ MUTANTS = {
     "flex_no_anchors": ("    sel = {0, nb - 1}.union(order[:k].tolist())", "    sel = set(order[:k].tolist())"),
     "median_with_anchors": ("        mu = float(np.median(p[1:nb - 1]))", "        mu = float(np.median(p))"),
     "band_wrong_side": ("        deltas = np.union1d(deltas, deltas + 1)", "        deltas = np.union1d(deltas, deltas - 1)"),
+    "pe_row_scaled_by_nb": ("            k_r, o_r, c_r = gamma_cumsum(a_bar[r, : r + 1], gamma)",
+                            "            k_r, o_r, c_r = gamma_cumsum(a_bar[r, : r + 1] / nb, gamma)"),
+    "pe_row_no_diagonal": ("        mask[np.diag_indices(nb)] = True\n", ""),
+    "pe_row_global_cut": ("            k_r, o_r, c_r = gamma_cumsum(a_bar[r, : r + 1], gamma)",
+                          "            k_r, o_r, c_r = gamma_cumsum(a_bar[r, : r + 1], gamma * (r + 1) / nb)"),
     "bf16_decode_shift": ("    w = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)",
                           "    w = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)"),
 }
