@@ -410,7 +410,8 @@ def main():
                 keep = (layer, rp, col, r)
                 if not args.no_variants:
                     c = layer.crisp
-                    for nm, bits in (("median_floor", c.VARIANT_MEDIAN_FLOOR), ("slash_band", c.VARIANT_SLASH_BAND)):
+                    for nm, bits in (("median_floor", c.VARIANT_MEDIAN_FLOOR), ("slash_band", c.VARIANT_SLASH_BAND),
+                                     ("pe_per_row", c.VARIANT_PE_PER_ROW)):
                         vr = layer.measure(a, 2, 1, variant=bits)
                         variants.append(dict(variant=nm, workload=vr["workload"], alpha=a,
                                              ms_per_layer=round(vr["ms_per_layer"], 3), stage_ms=vr["stage_ms"],

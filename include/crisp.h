@@ -175,9 +175,14 @@ int dense_attn(const crisp_shape* shape, const void* q_bf16, const void* k_bf16,
  * CRISP_VARIANT_SLASH_BAND: a selected slash block covers the token offsets
  *   128 delta .. 128 delta + 127, which reach the tiles of block diagonals
  *   delta and delta + 1; both are selected (the default selects delta only).
+ * CRISP_VARIANT_PE_PER_ROW: PE heads run the gamma-cumsum inside each query-
+ *   block row of the pooled map (each row a distribution over kb <= qb: the
+ *   row keeps its shortest descending prefix reaching gamma, ties to the lower
+ *   block, plus its diagonal) instead of over the whole flattened map (the
+ *   digest's PEIndex steps leave the flattening's extent open).
  * Everything else (arguments, workspace CRISP_CALL_SELECT, errors) is as for
  * crisp_select; unknown bits give CRISP_ERR_PARAM. */
-enum crisp_variant { CRISP_VARIANT_MEDIAN_FLOOR = 1, CRISP_VARIANT_SLASH_BAND = 2 };
+enum crisp_variant { CRISP_VARIANT_MEDIAN_FLOOR = 1, CRISP_VARIANT_SLASH_BAND = 2, CRISP_VARIANT_PE_PER_ROW = 4 };
 int crisp_select_variant(const crisp_shape* shape, const crisp_cfg* cfg, int variant, const void* q_bf16,
                          const void* k_bf16, const int8_t* pattern, const float* p_vert, const float* p_slash,
                          int64_t* row_ptr, int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws,

@@ -28,7 +28,7 @@ _LIB_PATH = os.path.join(_HERE, "libcrisp.so")
 _lib = None
 
 CALL_ROUTE, CALL_SELECT, CALL_ATTN, CALL_DENSE, CALL_FLEX_ROUTE, CALL_FLEX_SELECT = 0, 1, 2, 3, 4, 5
-VARIANT_MEDIAN_FLOOR, VARIANT_SLASH_BAND = 1, 2
+VARIANT_MEDIAN_FLOOR, VARIANT_SLASH_BAND, VARIANT_PE_PER_ROW = 1, 2, 4
 OUT_F32, OUT_BF16 = 0, 1
 
 
@@ -177,7 +177,7 @@ def select(q, k, routed: dict, cfg: Cfg | None = None, out: dict | None = None, 
            with_mask: bool = False, stream=None, _flex: bool = False, variant: int = 0) -> dict:
     """VSIndex / PEIndex: the selected block set as a CSR over (batch, head, query block).
 
-    ``variant``: bits VARIANT_MEDIAN_FLOOR / VARIANT_SLASH_BAND (crisp_select_variant)."""
+    ``variant``: bits VARIANT_MEDIAN_FLOOR / VARIANT_SLASH_BAND / VARIANT_PE_PER_ROW (crisp_select_variant)."""
     import torch
     cfg = cfg or config()
     _check_qkv(q, k)

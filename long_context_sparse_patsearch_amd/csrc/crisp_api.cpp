@@ -152,7 +152,7 @@ int crisp_route(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf
 static int select_common(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
                          const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
                          int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws, size_t ws_bytes,
-                         void* stream, int vs_rule, int band) {
+                         void* stream, int vs_rule, int band, int pe_rows = 0) {
   Dims dm;
   int st = make_dims(shape, &dm);
   if (st) return st;
@@ -169,7 +169,7 @@ static int select_common(const crisp_shape* shape, const crisp_cfg* cfg, const v
   return hip_status(crisp::launch_select(dm, cfg->alpha, cfg->gamma, cfg->k_min_tokens / kBlock,
                                          static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(k_bf16),
                                          pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask, w,
-                                         static_cast<hipStream_t>(stream), vs_rule, band));
+                                         static_cast<hipStream_t>(stream), vs_rule, band, pe_rows));
 }
 
 int crisp_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
@@ -184,10 +184,12 @@ int crisp_select_variant(const crisp_shape* shape, const crisp_cfg* cfg, int var
                          const void* k_bf16, const int8_t* pattern, const float* p_vert, const float* p_slash,
                          int64_t* row_ptr, int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws,
                          size_t ws_bytes, void* stream) {
-  if (variant & ~(CRISP_VARIANT_MEDIAN_FLOOR | CRISP_VARIANT_SLASH_BAND)) return CRISP_ERR_PARAM;
+  if (variant & ~(CRISP_VARIANT_MEDIAN_FLOOR | CRISP_VARIANT_SLASH_BAND | CRISP_VARIANT_PE_PER_ROW))
+    return CRISP_ERR_PARAM;
   const int rule = (variant & CRISP_VARIANT_MEDIAN_FLOOR) ? crisp::VS_MEDIAN_FLOOR : crisp::VS_NOISE_FLOOR;
   return select_common(shape, cfg, q_bf16, k_bf16, pattern, p_vert, p_slash, row_ptr, col_idx, col_capacity,
-                       sel_mask, ws, ws_bytes, stream, rule, (variant & CRISP_VARIANT_SLASH_BAND) ? 1 : 0);
+                       sel_mask, ws, ws_bytes, stream, rule, (variant & CRISP_VARIANT_SLASH_BAND) ? 1 : 0,
+                       (variant & CRISP_VARIANT_PE_PER_ROW) ? 1 : 0);
 }
 
 int flex_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,

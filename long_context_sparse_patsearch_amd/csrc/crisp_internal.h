@@ -37,6 +37,7 @@ struct SelectWs {
   int32_t* eqcnt;       // [rows]
   int32_t* seltake;     // [rows]
   int64_t* scan_part;   // [scan blocks + 1]
+  unsigned long long* pe_rowst;   // [rows][2] per-row cut of the per-row PE variant: key T, cells equal to T taken
 };
 size_t select_ws_layout(const Dims& dm, SelectWs* ws, char* base);
 // vs_rule: VS_NOISE_FLOOR (CRISP's VSIndex), VS_GAMMA_CUMSUM (FlexPrefill's budget rule) or
@@ -47,7 +48,7 @@ hipError_t launch_select(const Dims& dm, float alpha, float gamma, int kmin_bloc
                          const uint16_t* q, const uint16_t* k, const int8_t* pattern,
                          const float* p_vert, const float* p_slash, int64_t* row_ptr,
                          int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st,
-                         int vs_rule = VS_NOISE_FLOOR, int band = 0);
+                         int vs_rule = VS_NOISE_FLOOR, int band = 0, int pe_rows = 0);
 
 // ---- the FlexPrefill baseline path (flex.hip) ----
 // ws: flex_route_ws_bytes(dm) bytes (pooled keys of every KV group)

@@ -385,12 +385,93 @@ __global__ __launch_bounds__(NTHR) void pe_find_kernel(const int8_t* __restrict_
 }
 
 // ------------------------------------------------------------------------------------------------
+// Per-row PEIndex (variant): the gamma-cumsum inside each row of the pooled map, as the same
+// three-pass radix select run over one row per workgroup in LDS.  need = gamma / N_b in the
+// fixed point (a row of x = A_bar / N_b sums to 1 / N_b).  rowst[r] = {T, take}: the row keeps
+// its cells above T and its first `take` cells equal to T (~0: all of them).
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(NTHR) void pe_row_select_kernel(const int8_t* __restrict__ pattern,
+                                                             const float* __restrict__ abar, u64* __restrict__ rowst,
+                                                             int nb, int64_t tri, u64 need) {
+  __shared__ u64 lm[HBINS];
+  __shared__ u64 sh[3];   // prefix, mass above, done
+  const int qb = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (pattern[bh] != 0) return;
+  const int64_t r = bh * nb + qb;
+  const uint32_t* keys = reinterpret_cast<const uint32_t*>(abar + (size_t)bh * tri + tri_off(qb));
+  const int len = qb + 1;
+  const int tid = threadIdx.x, lane = lane_id();
+  if (tid == 0) { sh[0] = 0; sh[1] = 0; sh[2] = 0; }
+  for (int pass = 0; pass < 3; ++pass) {
+    int shift, width;
+    pass_bits(pass, shift, width);
+    const int pshift = shift + width;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int i = tid; i < HBINS; i += NTHR) lm[i] = 0;
+    __syncthreads();
+    const uint32_t prefix = (uint32_t)sh[0];
+    for (int e = tid; e < len; e += NTHR) {
+      const uint32_t key = keys[e];
+      if (pass > 0 && (key >> pshift) != prefix) continue;
+      atomicAdd(&lm[(key >> shift) & dmask], mass_fx(key));
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // buckets from the top: lane j owns buckets nbk-1-32j .. nbk-32-32j (nbk = 2^width <= 2048)
+      const int nbk = 1 << width, per = nbk / 64;
+      const u64 rem = need - sh[1];
+      u64 own = 0;
+      for (int i = 0; i < per; ++i) own += lm[nbk - 1 - per * lane - i];
+      u64 incl = own;   // inclusive prefix over lanes (top buckets first)
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const u64 v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      const u64 hit = __ballot(incl >= rem);
+      if (hit == 0) {
+        if (lane == 0) sh[2] = 1;   // the row sums to less than gamma: keep it all
+      } else {
+        const int j = __builtin_ctzll(hit);
+        if (lane == j) {
+          u64 cum = incl - own;
+          int found = nbk - 1 - per * lane;
+          for (int i = 0; i < per; ++i) {
+            const int bkt = nbk - 1 - per * lane - i;
+            if (cum + lm[bkt] >= rem) { found = bkt; break; }
+            cum += lm[bkt];
+          }
+          sh[0] = (sh[0] << width) | (u64)found;
+          sh[1] += cum;
+        }
+      }
+    }
+    __syncthreads();
+    if (sh[2]) break;
+  }
+  if (tid == 0) {
+    if (sh[2]) {
+      rowst[2 * r] = 0;
+      rowst[2 * r + 1] = ~0ull;
+    } else {
+      const uint32_t T = (uint32_t)sh[0];
+      const u64 rem = need - sh[1];
+      const u64 mt = mass_fx(T);
+      rowst[2 * r] = T;
+      rowst[2 * r + 1] = mt ? (rem + mt - 1) / mt : ~0ull;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // CSR: count per row, per-head tie allocation (PE), exclusive scan, fill.
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void row_count_kernel(const int8_t* __restrict__ pattern, const uint8_t* __restrict__ vsflags,
                                                        const float* __restrict__ abar, const u64* __restrict__ state,
                                                        int64_t* __restrict__ rowcnt, int32_t* __restrict__ eqcnt,
-                                                       int32_t* __restrict__ seltake, int nb, int64_t tri, int band) {
+                                                       int32_t* __restrict__ seltake, int nb, int64_t tri, int band,
+                                                       const u64* __restrict__ rowst) {
   const int64_t r = blockIdx.x;
   const int64_t bh = r / nb;
   const int qb = (int)(r % nb);
@@ -409,8 +490,7 @@ __global__ __launch_bounds__(64) void row_count_kernel(const int8_t* __restrict_
     if (lane == 0) { rowcnt[r] = cnt; eqcnt[r] = 0; seltake[r] = 0; }
     return;
   }
-  const u64* st = state + bh * ST_WORDS;
-  const uint32_t T = (uint32_t)st[ST_T];
+  const uint32_t T = rowst ? (uint32_t)rowst[2 * r] : (uint32_t)state[bh * ST_WORDS + ST_T];
   const uint32_t* keys = reinterpret_cast<const uint32_t*>(abar + (size_t)bh * tri + tri_off(qb));
   int gt = 0, eq = 0;
   for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
@@ -421,9 +501,19 @@ __global__ __launch_bounds__(64) void row_count_kernel(const int8_t* __restrict_
   }
   if (lane == 0) {
     const uint32_t dk = keys[qb];
-    rowcnt[r] = gt;
-    eqcnt[r] = eq;
-    seltake[r] = dk > T ? 2 : (dk == T ? 1 : 0);   // class of the diagonal cell, resolved by pe_ties_kernel
+    if (rowst) {
+      // per-row cut: the row's own ties, in block order; the diagonal is the row's last cell
+      const u64 take = rowst[2 * r + 1];
+      const int tk = take >= (u64)eq ? eq : (int)take;
+      const bool diag_sel = dk > T || (dk == T && eq <= tk);
+      rowcnt[r] = gt + tk + (diag_sel ? 0 : 1);
+      eqcnt[r] = eq;
+      seltake[r] = tk;
+    } else {
+      rowcnt[r] = gt;
+      eqcnt[r] = eq;
+      seltake[r] = dk > T ? 2 : (dk == T ? 1 : 0);   // class of the diagonal cell, resolved by pe_ties_kernel
+    }
   }
 }
 
@@ -535,7 +625,8 @@ __global__ __launch_bounds__(NTHR) void scan_apply_kernel(const int64_t* __restr
 __global__ __launch_bounds__(64) void fill_kernel(const int8_t* __restrict__ pattern, const uint8_t* __restrict__ vsflags,
                                                   const float* __restrict__ abar, const u64* __restrict__ state,
                                                   const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ seltake,
-                                                  int32_t* __restrict__ col_idx, int nb, int64_t tri, int band) {
+                                                  int32_t* __restrict__ col_idx, int nb, int64_t tri, int band,
+                                                  const u64* __restrict__ rowst) {
   const int64_t r = blockIdx.x;
   const int64_t bh = r / nb;
   const int qb = (int)(r % nb);
@@ -555,7 +646,7 @@ __global__ __launch_bounds__(64) void fill_kernel(const int8_t* __restrict__ pat
     }
     return;
   }
-  const uint32_t T = (uint32_t)state[bh * ST_WORDS + ST_T];
+  const uint32_t T = rowst ? (uint32_t)rowst[2 * r] : (uint32_t)state[bh * ST_WORDS + ST_T];
   const int take = seltake[r];
   const uint32_t* keys = reinterpret_cast<const uint32_t*>(abar + (size_t)bh * tri + tri_off(qb));
   int ties = 0;
@@ -578,7 +669,7 @@ template <int D>
 hipError_t select_impl(const Dims& dm, float alpha, float gamma, int kmin, const uint16_t* q, const uint16_t* k,
                        const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
                        int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st, int vs_rule,
-                       int band) {
+                       int band, int pe_rows) {
   const int nb = dm.nb;
   const unsigned bh = (unsigned)dm.bh;
   if (vs_rule == VS_GAMMA_CUMSUM) {
@@ -597,24 +688,34 @@ hipError_t select_impl(const Dims& dm, float alpha, float gamma, int kmin, const
   const float c2 = LOG2E / sqrtf((float)D);
   pe_logits_kernel<D><<<dim3(pairs, bh), NTHR, 0, st>>>(ws.qbar, ws.kbar, pattern, ws.abar, nb, dm.h_q, dm.group, dm.tri, c2);
   pe_softmax_kernel<<<dim3(nb, bh), NTHR, 0, st>>>(pattern, ws.abar, nb, dm.tri);
-  const u64 need = (u64)ceil((double)gamma * 0x1p60);
-  pe_state_init_kernel<<<(bh + 255) / 256, 256, 0, st>>>(pattern, ws.pe_state, dm.bh, need);
-  const unsigned hchunks = (unsigned)((dm.tri + HIST_CHUNK - 1) / HIST_CHUNK);
-  for (int pass = 0; pass < 3; ++pass) {
-    zero_u64_kernel<<<256, 256, 0, st>>>(ws.hist_mass, dm.bh * HBINS);
-    zero_u32_kernel<<<256, 256, 0, st>>>(ws.hist_cnt, dm.bh * HBINS);
-    pe_hist_kernel<<<dim3(hchunks, bh), NTHR, 0, st>>>(pattern, ws.abar, ws.pe_state, ws.hist_mass, ws.hist_cnt, dm.tri, pass);
-    pe_find_kernel<<<bh, NTHR, 0, st>>>(pattern, ws.hist_mass, ws.hist_cnt, ws.pe_state, pass);
+  const u64* rowst = nullptr;
+  if (pe_rows) {
+    const u64 need_row = (u64)ceil((double)gamma / (double)nb * 0x1p60);
+    pe_row_select_kernel<<<dim3(nb, bh), NTHR, 0, st>>>(pattern, ws.abar, ws.pe_rowst, nb, dm.tri, need_row);
+    rowst = ws.pe_rowst;
+    row_count_kernel<<<(unsigned)dm.rows, 64, 0, st>>>(pattern, ws.vsflags, ws.abar, ws.pe_state, ws.rowcnt, ws.eqcnt,
+                                                        ws.seltake, nb, dm.tri, band, rowst);
+  } else {
+    const u64 need = (u64)ceil((double)gamma * 0x1p60);
+    pe_state_init_kernel<<<(bh + 255) / 256, 256, 0, st>>>(pattern, ws.pe_state, dm.bh, need);
+    const unsigned hchunks = (unsigned)((dm.tri + HIST_CHUNK - 1) / HIST_CHUNK);
+    for (int pass = 0; pass < 3; ++pass) {
+      zero_u64_kernel<<<256, 256, 0, st>>>(ws.hist_mass, dm.bh * HBINS);
+      zero_u32_kernel<<<256, 256, 0, st>>>(ws.hist_cnt, dm.bh * HBINS);
+      pe_hist_kernel<<<dim3(hchunks, bh), NTHR, 0, st>>>(pattern, ws.abar, ws.pe_state, ws.hist_mass, ws.hist_cnt, dm.tri,
+                                                         pass);
+      pe_find_kernel<<<bh, NTHR, 0, st>>>(pattern, ws.hist_mass, ws.hist_cnt, ws.pe_state, pass);
+    }
+    row_count_kernel<<<(unsigned)dm.rows, 64, 0, st>>>(pattern, ws.vsflags, ws.abar, ws.pe_state, ws.rowcnt, ws.eqcnt,
+                                                        ws.seltake, nb, dm.tri, band, nullptr);
+    pe_ties_kernel<<<bh, NTHR, 0, st>>>(pattern, ws.pe_state, ws.rowcnt, ws.eqcnt, ws.seltake, nb);
   }
-  row_count_kernel<<<(unsigned)dm.rows, 64, 0, st>>>(pattern, ws.vsflags, ws.abar, ws.pe_state, ws.rowcnt, ws.eqcnt,
-                                                      ws.seltake, nb, dm.tri, band);
-  pe_ties_kernel<<<bh, NTHR, 0, st>>>(pattern, ws.pe_state, ws.rowcnt, ws.eqcnt, ws.seltake, nb);
   const int64_t nblk = (dm.rows + SCAN_PER - 1) / SCAN_PER;
   scan_blocks_kernel<<<(unsigned)nblk, NTHR, 0, st>>>(ws.rowcnt, ws.scan_part, dm.rows);
   scan_top_kernel<<<1, NTHR, 0, st>>>(ws.scan_part, nblk);
   scan_apply_kernel<<<(unsigned)nblk, NTHR, 0, st>>>(ws.rowcnt, ws.scan_part, row_ptr, dm.rows, nblk);
   fill_kernel<<<(unsigned)dm.rows, 64, 0, st>>>(pattern, ws.vsflags, ws.abar, ws.pe_state, row_ptr, ws.seltake, col_idx,
-                                                nb, dm.tri, band);
+                                                nb, dm.tri, band, rowst);
   return hipGetLastError();
 }
 
@@ -641,6 +742,7 @@ size_t select_ws_layout(const Dims& dm, SelectWs* ws, char* base) {
   w.eqcnt = (int32_t*)take((size_t)dm.rows * 4);
   w.seltake = (int32_t*)take((size_t)dm.rows * 4);
   w.scan_part = (int64_t*)take((size_t)((dm.rows + SCAN_PER - 1) / SCAN_PER + 1) * 8);
+  w.pe_rowst = (unsigned long long*)take((size_t)dm.rows * 16);
   if (ws) *ws = w;
   return off;
 }
@@ -648,12 +750,12 @@ size_t select_ws_layout(const Dims& dm, SelectWs* ws, char* base) {
 hipError_t launch_select(const Dims& dm, float alpha, float gamma, int kmin_blocks, const uint16_t* q, const uint16_t* k,
                          const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
                          int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st, int vs_rule,
-                         int band) {
+                         int band, int pe_rows) {
   if (dm.d == 128)
     return select_impl<128>(dm, alpha, gamma, kmin_blocks, q, k, pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask,
-                            ws, st, vs_rule, band);
+                            ws, st, vs_rule, band, pe_rows);
   return select_impl<64>(dm, alpha, gamma, kmin_blocks, q, k, pattern, p_vert, p_slash, row_ptr, col_idx, sel_mask, ws,
-                         st, vs_rule, band);
+                         st, vs_rule, band, pe_rows);
 }
 
 }  // namespace crisp

@@ -119,7 +119,35 @@ def check_vs(g, bh, r, alpha, kmin, nb, band=False):
                                         (set(np.nonzero(mask[1])[0]), set(r["sel_s"]))])
 
 
+def check_pe_rows(g, bh, r, gamma, nb):
+    """Per-row PE (R22): every row's set equals the oracle's, except cells on
+    that row's own cut (score or prefix within REL of the row's threshold)."""
+    assert not g["mask"][bh].any()
+    pe = r["pe"]
+    x = pe["x"]
+    got = rows_of(g, bh, nb)
+    ndiff = 0
+    for qb in range(nb):
+        a, b_ = set(got[qb].tolist()), set(pe["rows"][qb].tolist())
+        if a == b_:
+            continue
+        base = qb * (qb + 1) // 2
+        order, cs, kept = pe["row_order"][qb], pe["row_cs"][qb], pe["row_kept"][qb]
+        v = x[base: base + qb + 1] * nb
+        v_cut = v[kept[-1]]
+        rank = np.empty(qb + 1, dtype=np.int64)
+        rank[order] = np.arange(qb + 1)
+        for kb in a ^ b_:
+            before = cs[rank[kb] - 1] if rank[kb] > 0 else 0.0
+            ok = abs(v[kb] - v_cut) <= REL * v_cut or abs(before - gamma) <= REL * gamma
+            assert ok, (bh, qb, kb, v[kb], v_cut, before)
+            ndiff += 1
+    return ndiff
+
+
 def check_pe(g, bh, r, gamma, nb):
+    if r["pe"].get("per_row"):
+        return check_pe_rows(g, bh, r, gamma, nb)
     assert not g["mask"][bh].any()
     pe = r["pe"]
     x, order, cs = pe["x"], pe["order"], pe["cs"]
@@ -140,11 +168,12 @@ def check_pe(g, bh, r, gamma, nb):
     return ndiff
 
 
-def oracle_layer(inp, cfg_kw, force_vs=None, workers=None, floor="mean", band=False):
-    return layer_selection(inp["q"], inp["k"], force_vs=force_vs, workers=workers, floor=floor, band=band, **cfg_kw)
+def oracle_layer(inp, cfg_kw, force_vs=None, workers=None, floor="mean", band=False, pe_per_row=False):
+    return layer_selection(inp["q"], inp["k"], force_vs=force_vs, workers=workers, floor=floor, band=band,
+                           pe_per_row=pe_per_row, **cfg_kw)
 
 
-def check_selection(g, inp, ora, cfg_kw, H, nb, floor="mean", band=False):
+def check_selection(g, inp, ora, cfg_kw, H, nb, floor="mean", band=False, pe_per_row=False):
     """Route + select checks; returns the oracle dict actually compared (after re-runs)."""
     exempt = check_route(g, ora, H, cfg_kw["tau"])
     if exempt:
@@ -152,7 +181,7 @@ def check_selection(g, inp, ora, cfg_kw, H, nb, floor="mean", band=False):
         if redo:
             ora = dict(ora)
             ora.update(layer_selection(inp["q"], inp["k"], heads=list(redo), force_vs=redo, floor=floor,
-                                        band=band, **cfg_kw))
+                                        band=band, pe_per_row=pe_per_row, **cfg_kw))
     kmin = cfg_kw["k_min_tokens"] // 128
     stats = dict(vs_diff=0, pe_diff=0)
     for (b, h), r in ora.items():

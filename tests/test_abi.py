@@ -163,8 +163,9 @@ def test_select_variant_rejects_unknown_bits(lib):
     def call(variant, cap_=cap):
         return lib.crisp_select_variant(ctypes.byref(sh), ctypes.byref(cfg), variant, FAKE, FAKE, FAKE, FAKE, FAKE,
                                         FAKE, FAKE, cap_, None, FAKE, need, None)
-    assert call(4) == PARAM and call(-1) == PARAM
+    assert call(8) == PARAM and call(-1) == PARAM
     assert call(crisp.VARIANT_MEDIAN_FLOOR | crisp.VARIANT_SLASH_BAND, cap_=cap - 1) == CAP
+    assert call(crisp.VARIANT_PE_PER_ROW, cap_=cap - 1) == CAP
 
 
 def test_attention_rejects_before_any_hip_call(lib):

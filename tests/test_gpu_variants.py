@@ -1,6 +1,7 @@
-"""GPU parity of the VSIndex variants (median noise floor, slash band) against
-the oracle's crisp_head(floor=..., band=...): routing and selection in full;
-outputs in full on the 4k layer and on sampled blocks at 32k and 128k."""
+"""GPU parity of the selection variants (median noise floor, slash band,
+per-row PE gamma-cumsum) against the oracle's crisp_head(floor=..., band=...,
+pe_per_row=...): routing and selection in full; outputs in full on the 4k
+layer and on sampled blocks at 32k and 128k."""
 import numpy as np
 import pytest
 
@@ -11,15 +12,18 @@ from prefill_inputs import WORKLOADS, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = {"median": (crisp.VARIANT_MEDIAN_FLOOR, "median", False),
-            "band": (crisp.VARIANT_SLASH_BAND, "mean", True),
-            "median+band": (crisp.VARIANT_MEDIAN_FLOOR | crisp.VARIANT_SLASH_BAND, "median", True)}
+VARIANTS = {"median": (crisp.VARIANT_MEDIAN_FLOOR, "median", False, False),
+            "band": (crisp.VARIANT_SLASH_BAND, "mean", True, False),
+            "median+band": (crisp.VARIANT_MEDIAN_FLOOR | crisp.VARIANT_SLASH_BAND, "median", True, False),
+            "pe_row": (crisp.VARIANT_PE_PER_ROW, "mean", False, True),
+            "all": (crisp.VARIANT_MEDIAN_FLOOR | crisp.VARIANT_SLASH_BAND | crisp.VARIANT_PE_PER_ROW, "median", True,
+                    True)}
 CASES = [(i, v) for i in (1, 2, 3) for v in VARIANTS]
 
 
 @pytest.mark.parametrize("idx,name", CASES, ids=[f"{WORKLOADS[i].name}-{v}" for i, v in CASES])
 def test_variant_parity(idx, name):
-    variant, floor, band = VARIANTS[name]
+    variant, floor, band, pe_rows = VARIANTS[name]
     wl = WORKLOADS[idx]
     sh = wl.shape
     nb = sh.n_blocks
@@ -29,8 +33,8 @@ def test_variant_parity(idx, name):
     ckw = cfg_kwargs(cfg)
     g = gpu_layer(q, k, v, cfg, variant=variant)
     check_csr_structure(g, sh.batch * sh.h_q, nb, crisp.max_blocks(crisp.shape_of(q, k)))
-    ora = oracle_layer(inp, ckw, floor=floor, band=band)
-    ora, stats = check_selection(g, inp, ora, ckw, sh.h_q, nb, floor=floor, band=band)
+    ora = oracle_layer(inp, ckw, floor=floor, band=band, pe_per_row=pe_rows)
+    ora, stats = check_selection(g, inp, ora, ckw, sh.h_q, nb, floor=floor, band=band, pe_per_row=pe_rows)
     print(f"[{wl.name} {name}] selection ok: tiles={int(g['row_ptr'][-1])} diffs={stats}", flush=True)
     rng = np.random.default_rng(200 + idx)
     blocks = {bh: (range(nb) if idx == 1 else sample_blocks(nb, rng)) for bh in ora}
