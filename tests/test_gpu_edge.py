@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = {
     "minimal_nb3_d64": Shape(1, 384, 1, 1, 64),
+    "minimal_nb3_d128": Shape(1, 384, 2, 1, 128),
     "ragged_nb9_b2_g2": Shape(2, 1152, 4, 2, 128),
     "gqa7_nb16": Shape(1, 2048, 7, 1, 128),
     "mha_nb32_d64": Shape(1, 4096, 2, 2, 64),
@@ -54,7 +55,8 @@ def test_dense_attention_full(name):
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_sparse_attention_on_given_csr(name):
     """Random CSR rows (some without the diagonal, some empty, some holding
-    blocks after the query block or past the end) against the oracle."""
+    blocks after the query block or past the end, some opening with 70 such
+    entries, more than one 64-entry read) against the oracle."""
     sh = SHAPES[name]
     nb = sh.n_blocks
     inp = _inputs(sh, seed=31)
@@ -65,7 +67,7 @@ def test_sparse_attention_on_given_csr(name):
         for h in range(sh.h_q):
             per = []
             for qb in range(nb):
-                kind = rng.integers(0, 6)
+                kind = rng.integers(0, 7)
                 if kind == 0:
                     row = []
                 elif kind == 1:
@@ -76,6 +78,8 @@ def test_sparse_attention_on_given_csr(name):
                     row = row + [qb + 1]          # a future block: fully masked
                 if kind == 4:
                     row = row + [nb]              # past the end: skipped
+                if kind == 6:
+                    row = [nb if i % 2 else min(qb + 1, nb) for i in range(70)] + row   # skipped, then valid
                 per.append(row)
             rows_all.extend(per)
             rows_oracle[(b, h)] = [np.array([c for c in r if c < nb], dtype=np.int64) for r in per]
@@ -90,6 +94,7 @@ def test_sparse_attention_on_given_csr(name):
 
 CASES = [
     ("minimal_nb3_d64", {}),
+    ("minimal_nb3_d128", {}),
     ("ragged_nb9_b2_g2", {}),
     ("gqa7_nb16", {}),
     ("mha_nb32_d64", {}),
