@@ -1005,14 +1005,14 @@ hipError_t attn_launch(const Dims& dm, const uint16_t* q, const uint16_t* k, con
     else
       attn_q64_kernel<DENSE, false><<<grid64, Q64_THR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
                                                                 dm.group, qd, counters, c2);
-    return hipGetLastError();
+  } else {
+    if (out_bf16)
+      attn_kernel<D, DENSE, true><<<grid, NTHR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
+                                                         dm.group, qd, counters, c2);
+    else
+      attn_kernel<D, DENSE, false><<<grid, NTHR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
+                                                          dm.group, qd, counters, c2);
   }
-  if (out_bf16)
-    attn_kernel<D, DENSE, true><<<grid, NTHR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
-                                                       dm.group, qd, counters, c2);
-  else
-    attn_kernel<D, DENSE, false><<<grid, NTHR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
-                                                        dm.group, qd, counters, c2);
   return hipGetLastError();
 }
 
