@@ -515,6 +515,16 @@ __device__ __forceinline__ void mfma_drain() {
   fence();
 }
 
+// Barriers of the stage loop.  Every direct load of a stage is 8 instructions
+// per wave, and each barrier waits for a stage load that has exactly two stage
+// loads (16 instructions) issued after it, so both wait for vmcnt <= 16.
+__device__ __forceinline__ void bar_top() {
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void bar_mid() {
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // max / sum over lanes l and l ^ 32
 __device__ __forceinline__ float halves_max(float t) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
@@ -559,11 +569,11 @@ __device__ __forceinline__ void q64_pair_prog(Q64Soft& sm, const f32x16 (&sc)[2]
 // with i = 2 (8 ks + st) + t; operand read r = 8 ks + st feeds MFMAs 2r, 2r+1.
 // The read stream continues into the PV phase: reads 16..19 are its first V^T
 // operands (the V^T stage is already resident).
-template <bool HAS_NEXT>
+template <bool HAS_NEXT, typename Mid>
 __device__ __forceinline__ void q64_qk(const char* kbase, const char* vbase, const uint32_t (&koff)[8],
                                        const uint32_t (&voff)[4], const u32x4 (&qf)[2][8], f32x16 (&sn)[2][2],
                                        const f32x16 (&sc)[2][2], float c2, const float (&nm)[2], Q64Soft& sm,
-                                       float (&l)[2], u32x4 (&op)[Q64_AHEAD + 1]) {
+                                       float (&l)[2], u32x4 (&op)[Q64_AHEAD + 1], Mid&& mid) {
   constexpr int KROW = 256, VROW = KS * 2;
   constexpr int NOPS = Q64_P1 * 2 * 7;
   auto read = [&](int r) -> u32x4 {
@@ -579,6 +589,8 @@ __device__ __forceinline__ void q64_qk(const char* kbase, const char* vbase, con
 #pragma unroll
     for (int q = (i * NOPS) / 32; q < ((i + 1) * NOPS) / 32; ++q) q64_pair_prog(sm, sc, 0, q, c2, nm, l);
     const int r = i >> 1;
+    // the stage's K reads are all issued; the mid-step barrier comes before the first V^T read
+    if (i == 2 * (16 - Q64_AHEAD)) mid();
     if (!(i & 1)) op[(r + Q64_AHEAD) % (Q64_AHEAD + 1)] = read(r + Q64_AHEAD);
     if (HAS_NEXT) {
       const int t = i & 1, ks = r >> 3, st = r & 7;
@@ -824,18 +836,24 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
     int64_t pc = next_valid(t0);
     if (pc < t1) {
+      // Stage s = (block, half).  K(s) lives in K buffer s % 2, V^T(s) in V buffer s % 2.
+      // Step s: QK of stage s+1 (phase 1), PV of stage s (phase 2).  Loads: V^T(s+1)
+      // after the step's top barrier, K(s+3) after its mid barrier (once every wave
+      // has read K(s+1)), so each load has a step and a half to land.  Loads past the
+      // row's end are dummies (the current block), which keeps the wait counts exact.
       int kb = entry(pc);
       int64_t pn = next_valid(pc + 1);
       int kbn = pn < t1 ? entry(pn) : -1;
+      int64_t pnn = kbn >= 0 ? next_valid(pn + 1) : t1;
+      int kbnn = pnn < t1 ? entry(pnn) : -1;
       f32x16 sa[2][2], sb[2][2];
       Q64Soft sm;
       u32x4 op[Q64_AHEAD + 1];
       float tm[2];
       issue_k(kb, 0, LK0);
-      vm_wait();
-      __syncthreads();
       issue_k(kb, 1, LK1);
       issue_v(kb, 0, LV0);
+      bar_top();   // K(kb, 0) landed for every wave
       fence();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -848,6 +866,9 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
           mfma_s(sa[1][r >> 3], kop, qf[1][r & 7]);
         }
       }
+      fence();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // every wave has read K(kb, 0)
+      issue_k(kbn >= 0 ? kbn : kb, 0, LK0);
       mfma_drain();
       if (kb == qb) {
         mask_diag(sa[0], 0, qloc0, lane);
@@ -865,15 +886,16 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
       q64_update(tm, c2, m, corr, any);
       for (;;) {
         // step A: current = (kb, 0) in sa, next = (kb, 1) -> sb
-        vm_wait();
-        __syncthreads();
-        if (kbn >= 0) issue_k(kbn, 0, LK0);
+        bar_top();                      // K(kb, 1) landed
         issue_v(kb, 1, LV1);
         l[0] *= corr[0];
         l[1] *= corr[1];
         {
           const float nm[2] = {-m[0], -m[1]};
-          q64_qk<true>(kbuf1, vbuf0, koff, voff, qf, sb, sa, c2, nm, sm, l, op);
+          q64_qk<true>(kbuf1, vbuf0, koff, voff, qf, sb, sa, c2, nm, sm, l, op, [&]() {
+            bar_mid();                  // V(kb, 0) landed; every wave has read K(kb, 1)
+            issue_k(kbn >= 0 ? kbn : kb, 1, LK1);
+          });
           q64_rescale(o, corr, any);
           if (kb == qb) q64_mask(sb, KS, qloc0, lane);
           q64_pv<true>(vbuf0, voff, o, sa, c2, nm, sm, l, sb, tm, op);
@@ -881,17 +903,16 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
         q64_update(tm, c2, m, corr, any);
 
         // step B: current = (kb, 1) in sb, next = (kbn, 0) -> sa
-        vm_wait();
-        __syncthreads();
+        bar_top();                      // K(kbn, 0) landed
+        issue_v(kbn >= 0 ? kbn : kb, 0, LV0);
         l[0] *= corr[0];
         l[1] *= corr[1];
-        if (kbn >= 0) {
-          issue_k(kbn, 1, LK1);
-          issue_v(kbn, 0, LV0);
-        }
         {
           const float nm[2] = {-m[0], -m[1]};
-          q64_qk<true>(kbuf0, vbuf1, koff, voff, qf, sa, sb, c2, nm, sm, l, op);
+          q64_qk<true>(kbuf0, vbuf1, koff, voff, qf, sa, sb, c2, nm, sm, l, op, [&]() {
+            bar_mid();                  // V(kb, 1) landed; every wave has read K(kbn, 0)
+            issue_k(kbnn >= 0 ? kbnn : kb, 0, LK0);
+          });
           q64_rescale(o, corr, any);
           if (kbn == qb) q64_mask(sa, 0, qloc0, lane);
           q64_pv<true>(vbuf1, voff, o, sb, c2, nm, sm, l, sa, tm, op);
@@ -899,9 +920,10 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
         if (kbn < 0) break;
         q64_update(tm, c2, m, corr, any);
         kb = kbn;
-        pc = pn;
-        pn = next_valid(pc + 1);
-        kbn = pn < t1 ? entry(pn) : -1;
+        pn = pnn;
+        kbn = kbnn;
+        pnn = kbn >= 0 ? next_valid(pn + 1) : t1;
+        kbnn = pnn < t1 ? entry(pnn) : -1;
       }
       mfma_drain();
     }
