@@ -1,10 +1,11 @@
 """GPU parity on the five single-layer workloads at full size.
 
 Routing and selection are compared in full on every head.  Outputs are
-compared in full where the fp64 oracle finishes in seconds (the tiny layer)
-and on sampled query blocks and rows elsewhere (first, middle, last and one
-random block per head; at 256k-512k tokens, 8 sampled rows per block), always
-against the oracle's attention on the GPU's own CSR.  The dense kernel is
+compared in full on the 4k and 32k layers; on the 128k layer every block of
+one VS and one PE head and sampled blocks of the others; elsewhere on sampled
+query blocks and rows (first, middle, last and one random block per head; at
+256k-512k tokens, 8 sampled rows per block), always against the oracle's
+attention on the GPU's own CSR.  The dense kernel is
 checked the same way.  Launch configuration is the one the benchmark times.
 """
 import gc
@@ -59,11 +60,15 @@ def test_layer_parity(idx, alpha):
     tiles = int(g["row_ptr"][-1])
     _log(f"[{wl.name} alpha={alpha}] selection ok: tiles={tiles} exempt diffs={stats}")
     rng = np.random.default_rng(idx * 10 + int(alpha * 100))
-    if idx == 1:
+    if idx in (1, 2):
         blocks = {bh: range(nb) for bh in ora}
         q_rows = None
     else:
         blocks = {bh: sample_blocks(nb, rng) for bh in ora}
+        if idx == 3:
+            for want in (True, False):   # one whole VS head and one whole PE head
+                bh = next(x for x in sorted(ora) if ora[x]["is_vs"] == want)
+                blocks[bh] = range(nb)
         q_rows = None if sh.n <= 131072 else np.unique(np.concatenate([[0, 1, 63, 64, 126, 127],
                                                                        rng.integers(0, 128, 2)]))
     rows = {bh: rows_of(g, bh[0] * sh.h_q + bh[1], nb) for bh in ora}
