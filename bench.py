@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flex", action="store_true", help="skip the FlexPrefill baseline path")
+    ap.add_argument("--no-probe", action="store_true", help="skip the measured MFMA-rate probe")
     ap.add_argument("--no-variants", action="store_true", help="skip the VSIndex variants (median floor, slash band)")
     ap.add_argument("--tau-jsd", type=float, default=0.1, help="JSD threshold of the FlexPrefill router")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -215,6 +216,30 @@ class Layer:
         for name in ("q", "k", "v", "o", "ws_r", "ws_s", "s_out", "r_out", "f_out", "ws_f"):
             setattr(self, name, None)
         torch.cuda.empty_cache()
+
+
+def mfma_rate():
+    """The bf16 MFMA rate this GPU sustains (crisp_mfma_probe, two waves per SIMD on every CU),
+    with random bf16 operands in [-2, 2) and with zeros; HIP events on the current stream."""
+    import torch
+    import long_context_sparse_patsearch_amd as crisp
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    out = {}
+    for name, ops in (("random_operands", torch.empty(crisp.PROBE_OPERAND_BYTES // 2, dtype=torch.bfloat16,
+                                                      device=dev).uniform_(-2.0, 2.0, generator=g)),
+                      ("zero_operands", torch.zeros(crisp.PROBE_OPERAND_BYTES // 2, dtype=torch.bfloat16, device=dev))):
+        crisp.mfma_probe(ops, iters=2000)
+        torch.cuda.synchronize()
+        e0, e1 = _event(), _event()
+        e0.record()
+        flop = crisp.mfma_probe(ops, iters=20000)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_tflops"] = round(flop / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    out["published_tflops"] = PEAK_BF16_TFLOPS
+    return out
 
 
 def cpu_baseline(layer, res, rp, col):
@@ -493,6 +518,11 @@ def main():
         out["flexprefill"] = flex
     if variants:
         out["variants"] = variants
+    if not args.no_probe:
+        mr = mfma_rate()
+        mr["attn_frac_of_random_operand_rate"] = round(tflops / mr["random_operands_tflops"], 4)
+        out["mfma_rate_measured"] = mr
+        log(f"[bench] measured MFMA rate: {mr}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(layer, res, rp, col)

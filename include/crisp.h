@@ -232,6 +232,21 @@ int flex_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf
  * as for the other calls.  Pure host logic; returns a status. */
 int crisp_use_dense(const crisp_shape* shape, int32_t* use_dense);
 
+/* ---- measurement: the sustained bf16 MFMA rate of this GPU ----
+ * For callers that report a kernel against the MFMA roofline of the running
+ * part (the benchmark).  Launches one workgroup of 512 threads per CU (two
+ * waves per SIMD); each wave issues 32 v_mfma_f32_32x32x16_bf16 per iteration
+ * on register operands loaded from `operands` (device, CRISP_PROBE_OPERAND_BYTES
+ * bytes of bf16 values chosen by the caller: the sustained rate of a
+ * power-limited part depends on the data).  Workgroup i writes one float to
+ * sink[i % CRISP_PROBE_SINK_FLOATS] (device).  *flop (host) receives the work
+ * of the launch (32768 FLOP per MFMA); the caller times the launch on
+ * `stream`.  Errors: CRISP_ERR_NULL, CRISP_ERR_ALIGN (16-byte operands, 4-byte
+ * sink), CRISP_ERR_PARAM (iters outside [1, 10^7]), CRISP_ERR_HIP. */
+#define CRISP_PROBE_OPERAND_BYTES 65536
+#define CRISP_PROBE_SINK_FLOATS 4096
+int crisp_mfma_probe(const void* operands, float* sink, int iters, double* flop, void* stream);
+
 /* Static description of a status code. */
 const char* crisp_status_string(int status);
 

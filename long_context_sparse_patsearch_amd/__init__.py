@@ -74,11 +74,13 @@ def load():
     lib.flex_route.argtypes = [ps, pc, ctypes.c_float, P, P, P, P, P, P, SZ, P]
     lib.flex_select.argtypes = [ps, pc, P, P, P, P, P, P, P, I64, P, P, SZ, P]
     lib.crisp_select_variant.argtypes = [ps, pc, I, P, P, P, P, P, P, P, I64, P, P, SZ, P]
+    lib.crisp_mfma_probe.argtypes = [P, P, I, ctypes.POINTER(ctypes.c_double), P]
     lib.crisp_status_string.argtypes = [I]
     lib.crisp_status_string.restype = ctypes.c_char_p
     lib.crisp_last_error.restype = ctypes.c_char_p
     for f in ("crisp_workspace_bytes", "crisp_max_blocks", "crisp_use_dense", "crisp_route", "crisp_select",
-              "crisp_sparse_attn", "dense_attn", "flex_route", "flex_select", "crisp_select_variant"):
+              "crisp_sparse_attn", "dense_attn", "flex_route", "flex_select", "crisp_select_variant",
+              "crisp_mfma_probe"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -264,6 +266,23 @@ def dense_attn(q, k, v, out=None, out_dtype=None, ws=None, stream=None):
     _check(load().dense_attn(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(out), code, _ptr(ws), nws,
                              _stream(stream)))
     return out
+
+
+PROBE_OPERAND_BYTES, PROBE_SINK_FLOATS = 65536, 4096
+
+
+def mfma_probe(operands, iters: int = 20000, sink=None, stream=None) -> float:
+    """Launch the sustained-MFMA-rate probe (crisp_mfma_probe) on ``operands``, a
+    device tensor of PROBE_OPERAND_BYTES bytes of bf16 values; returns the
+    launch's FLOP.  The caller times the launch on ``stream``."""
+    import torch
+    if operands.device.type != "cuda" or operands.numel() * operands.element_size() != PROBE_OPERAND_BYTES:
+        raise CrispError(-3, "operands must be a device tensor of PROBE_OPERAND_BYTES bytes")
+    if sink is None:
+        sink = torch.empty(PROBE_SINK_FLOATS, dtype=torch.float32, device=operands.device)
+    flop = ctypes.c_double(0.0)
+    _check(load().crisp_mfma_probe(_ptr(operands), _ptr(sink), int(iters), ctypes.byref(flop), _stream(stream)))
+    return flop.value
 
 
 def prefill(q, k, v, cfg: Cfg | None = None, out_dtype=None, stream=None, gate: bool = True) -> dict:

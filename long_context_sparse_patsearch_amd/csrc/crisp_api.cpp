@@ -259,6 +259,14 @@ int dense_attn(const crisp_shape* shape, const void* q_bf16, const void* k_bf16,
                                              out_dtype == CRISP_OUT_BF16, ws, static_cast<hipStream_t>(stream)));
 }
 
+int crisp_mfma_probe(const void* operands, float* sink, int iters, double* flop, void* stream) {
+  if (!operands || !sink || !flop) return CRISP_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(operands) % 16 || reinterpret_cast<uintptr_t>(sink) % 4) return CRISP_ERR_ALIGN;
+  if (iters < 1 || iters > 10000000) return CRISP_ERR_PARAM;
+  static_assert(crisp::PROBE_SINK_FLOATS == CRISP_PROBE_SINK_FLOATS, "sink size");
+  return hip_status(crisp::launch_mfma_probe(operands, sink, iters, flop, static_cast<hipStream_t>(stream)));
+}
+
 const char* crisp_status_string(int status) {
   switch (status) {
     case CRISP_OK: return "ok";

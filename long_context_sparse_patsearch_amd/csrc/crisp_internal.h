@@ -50,6 +50,11 @@ hipError_t launch_select(const Dims& dm, float alpha, float gamma, int kmin_bloc
                          int32_t* col_idx, uint8_t* sel_mask, const SelectWs& ws, hipStream_t st,
                          int vs_rule = VS_NOISE_FLOOR, int band = 0, int pe_rows = 0);
 
+// ---- measurement (probe.hip) ----
+constexpr int PROBE_SINK_FLOATS = 4096;
+// flop: the launch's work (host); operands: 65536 bytes of bf16 pairs (device)
+hipError_t launch_mfma_probe(const void* operands, float* sink, int iters, double* flop, hipStream_t st);
+
 // ---- the FlexPrefill baseline path (flex.hip) ----
 // ws: flex_route_ws_bytes(dm) bytes (pooled keys of every KV group)
 size_t flex_route_ws_bytes(const Dims& dm);

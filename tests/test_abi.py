@@ -204,3 +204,13 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(crisp, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(crisp.CrispError):
         crisp.load()
+
+
+def test_mfma_probe_rejects_before_any_hip_call(lib):
+    flop = ctypes.c_double(0.0)
+    assert lib.crisp_mfma_probe(None, FAKE, 10, ctypes.byref(flop), None) == NULL
+    assert lib.crisp_mfma_probe(FAKE, None, 10, ctypes.byref(flop), None) == NULL
+    assert lib.crisp_mfma_probe(FAKE, FAKE, 10, None, None) == NULL
+    assert lib.crisp_mfma_probe(FAKE + 8, FAKE, 10, ctypes.byref(flop), None) == ALIGN
+    assert lib.crisp_mfma_probe(FAKE, FAKE, 0, ctypes.byref(flop), None) == PARAM
+    assert lib.crisp_mfma_probe(FAKE, FAKE, 10 ** 7 + 1, ctypes.byref(flop), None) == PARAM
