@@ -34,8 +34,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama512k", help="|".join(ALIASES))
     ap.add_argument("--alpha", type=float, default=None, help="default: the workload's first setting")
     ap.add_argument("--also", default="llama512k@1.25,llama512k@1.5,llama128k,llama128k@1.25",
@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flex", action="store_true", help="skip the FlexPrefill baseline path")
     ap.add_argument("--no-probe", action="store_true", help="skip the measured MFMA-rate probe")
-    ap.add_argument("--no-variants", action="store_true", help="skip the VSIndex variants (median floor, slash band)")
+    ap.add_argument("--no-variants", action="store_true", help="skip the selection variants (median floor, slash band, per-row PE)")
     ap.add_argument("--tau-jsd", type=float, default=0.1, help="JSD threshold of the FlexPrefill router")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per attention launch (JSON), if current")
