@@ -86,9 +86,13 @@ struct Queue {
   int per_queue;           // items per queue
 };
 
+// Chunk length: N_b / 32 query blocks, at most 16 up to N_b = 1024 and at most
+// 32 above (measured on the 128k, 256k and 512k layers; a length that does not
+// split an XCD's 64 workgroups evenly over heads, such as 24, is slower at all three).
 inline int queue_chunk(int nb) {
-  int qc = nb / 32;
-  return qc < 1 ? 1 : (qc > 32 ? 32 : qc);
+  const int cap = nb <= 1024 ? 16 : 32;
+  const int qc = nb / 32;
+  return qc < 1 ? 1 : (qc > cap ? cap : qc);
 }
 
 inline Queue make_queue(int nb, int64_t bh_total) {
