@@ -14,7 +14,8 @@
 // free.  S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA; the online
 // softmax stays in fp32 registers (each lane owns one query column), with the
 // 1/sqrt(d)*log2(e) scale folded into one FMA feeding exp2 and the output
-// rescaled only in stages where some row maximum grows.  Items come from
+// rescaled only in stages where some row maximum outgrows its reference by
+// more than 2^8.  Items come from
 // per-XCD work queues (see Queue).
 //
 // Two kernels share this frame.  d = 128 (attn_q64_kernel): two waves per
@@ -35,7 +36,11 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr int NXCD = 8;                  // accelerator complex dies of an MI355X
 constexpr int KS = 64;                   // keys per pipeline stage
 constexpr int WG_PER_CU = 2;
-constexpr float RESCALE_LOG2 = 0.f;      // rescale whenever a row maximum grows (keeps the max weight exactly 1)
+// A row's reference maximum m is raised (and its output rescaled) only when a
+// stage's maximum exceeds it by more than 2^8, so weights 2^(s c2 - m) stay
+// <= 256.  The result is the same softmax: the row sum is taken over the same
+// bf16-rounded weights the PV product uses, so the choice of m cancels.
+constexpr float RESCALE_LOG2 = 8.f;
 constexpr float M_INIT = -1e30f;         // running-max sentinel (finite: keeps fma/exp2 NaN-free)
 
 template <int D>
@@ -482,7 +487,10 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
 // most one operand read, and one MFMA.  The softmax of a stage is split
 // between the QK phase (weight pairs [0, Q64_P1) of each tile) and the PV
 // phase (the rest, done by the time the PV MFMAs need them, then the next
-// stage's row maxima).
+// stage's row maxima).  The row sums come from the matrix cores as well: after
+// the PV MFMAs of a 16-key chunk, one 16x16x32 MFMA multiplies a constant 0/1
+// selector with that chunk's weight operand, which adds the chunk's bf16
+// weights of each query row into a 4-register accumulator in that row's lanes.
 //
 // The compiler does not see the MFMAs inside the asm, so the wait states the
 // hardware needs around them are kept by construction: a weight pair is
@@ -497,6 +505,7 @@ constexpr int Q64_P1 = 10;         // weight pairs per tile computed in the QK p
 constexpr int Q64_AHEAD = 4;       // operand reads in flight ahead of the MFMAs
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 lds16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -510,6 +519,11 @@ __device__ __forceinline__ void mfma_s(f32x16& s, const u32x4& a, const u32x4& b
 // o += V^T P^T tile product, o in AGPRs
 __device__ __forceinline__ void mfma_o(f32x16& o, const u32x4& a, const u32x4& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
+}
+// ls += SEL W: row sums of one 16-key chunk of weights (W, the B operand of the
+// PV MFMAs), ls and the selector in AGPRs
+__device__ __forceinline__ void mfma_l(f32x4& ls, const u32x4& sel, const u32x4& w) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(ls) : "a"(sel), "v"(w));
 }
 // 13 wait states: covers an MFMA result read by VALU code (or its accumulator
 // overwritten by VALU code) right after the MFMA
@@ -529,44 +543,39 @@ __device__ __forceinline__ void bar_mid() {
   asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// max / sum over lanes l and l ^ 32
+// max over lanes l and l ^ 32
 __device__ __forceinline__ float halves_max(float t) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float halves_sum(float t) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Softmax state of one stage for both tiles.  Weight pair p of tile t covers
 // accumulator registers 2p, 2p+1 (ks = p / 8) and becomes 32-bit word p % 4 of
-// the PV operand pw[t][p / 4]; its seven VALU ops are numbered k = 0..6: two
-// FMAs, two exp2, the bf16 pack, and two adds of the fp32 weights into the row
-// sum (plain adds: a v_dot2 here would wait for the MFMA in flight).
+// the PV operand pw[t][p / 4]; its five VALU ops are numbered k = 0..4: two
+// FMAs, two exp2 and the bf16 pack.
 struct Q64Soft {
   float a0[2][16], a1[2][16];
   u32x4 pw[2][4];
 };
 
+constexpr int Q64_PAIR_OPS = 5;
+
 __device__ __forceinline__ void q64_pair_op(Q64Soft& sm, const f32x16 (&sc)[2][2], int t, int p, int k, float c2,
-                                            const float (&nm)[2], float (&l)[2]) {
+                                            const float (&nm)[2]) {
   const int ks = p >> 3, r = (2 * p) & 15;
   switch (k) {
     case 0: sm.a0[t][p] = fmaf(sc[t][ks][r], c2, nm[t]); break;
     case 1: sm.a1[t][p] = fmaf(sc[t][ks][r + 1], c2, nm[t]); break;
     case 2: sm.a0[t][p] = fast_exp2(sm.a0[t][p]); break;
     case 3: sm.a1[t][p] = fast_exp2(sm.a1[t][p]); break;
-    case 4: sm.pw[t][p >> 2][p & 3] = pack_bf16x2(sm.a0[t][p], sm.a1[t][p]); break;
-    case 5: l[t] += sm.a0[t][p]; break;
-    default: l[t] += sm.a1[t][p];
+    default: sm.pw[t][p >> 2][p & 3] = pack_bf16x2(sm.a0[t][p], sm.a1[t][p]);
   }
 }
 // op q of the pair program over pairs [p0, p0 + np) of both tiles (pair-major, tiles alternating)
 __device__ __forceinline__ void q64_pair_prog(Q64Soft& sm, const f32x16 (&sc)[2][2], int p0, int q, float c2,
-                                              const float (&nm)[2], float (&l)[2]) {
-  const int pp = q / 7, k = q % 7;
-  q64_pair_op(sm, sc, pp & 1, p0 + (pp >> 1), k, c2, nm, l);
+                                              const float (&nm)[2]) {
+  const int pp = q / Q64_PAIR_OPS, k = q % Q64_PAIR_OPS;
+  q64_pair_op(sm, sc, pp & 1, p0 + (pp >> 1), k, c2, nm);
 }
 
 // QK phase.  Regions i = 0..31: MFMA i is S_n[t][ks] += K[ks][st] Q[t][st]^T
@@ -577,9 +586,9 @@ template <bool HAS_NEXT, typename Mid>
 __device__ __forceinline__ void q64_qk(const char* kbase, const char* vbase, const uint32_t (&koff)[8],
                                        const uint32_t (&voff)[4], const u32x4 (&qf)[2][8], f32x16 (&sn)[2][2],
                                        const f32x16 (&sc)[2][2], float c2, const float (&nm)[2], Q64Soft& sm,
-                                       float (&l)[2], u32x4 (&op)[Q64_AHEAD + 1], Mid&& mid) {
+                                       u32x4 (&op)[Q64_AHEAD + 1], Mid&& mid) {
   constexpr int KROW = 256, VROW = KS * 2;
-  constexpr int NOPS = Q64_P1 * 2 * 7;
+  constexpr int NOPS = Q64_P1 * 2 * Q64_PAIR_OPS;
   auto read = [&](int r) -> u32x4 {
     if (r < 16) return lds16(kbase + koff[r & 7] + 32 * (r >> 3) * KROW);
     const int v = r - 16;
@@ -591,7 +600,7 @@ __device__ __forceinline__ void q64_qk(const char* kbase, const char* vbase, con
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
 #pragma unroll
-    for (int q = (i * NOPS) / 32; q < ((i + 1) * NOPS) / 32; ++q) q64_pair_prog(sm, sc, 0, q, c2, nm, l);
+    for (int q = (i * NOPS) / 32; q < ((i + 1) * NOPS) / 32; ++q) q64_pair_prog(sm, sc, 0, q, c2, nm);
     const int r = i >> 1;
     // the stage's K reads are all issued; the mid-step barrier comes before the first V^T read
     if (i == 2 * (16 - Q64_AHEAD)) mid();
@@ -606,27 +615,29 @@ __device__ __forceinline__ void q64_qk(const char* kbase, const char* vbase, con
   // keep the weights computed here in this phase
 #pragma unroll
   for (int t = 0; t < 2; ++t)
-    asm volatile("" ::"v"(sm.pw[t][0]), "v"(sm.pw[t][1]), "v"(sm.pw[t][2][0]), "v"(sm.pw[t][2][1]), "v"(l[t]));
+    asm volatile("" ::"v"(sm.pw[t][0]), "v"(sm.pw[t][1]), "v"(sm.pw[t][2][0]), "v"(sm.pw[t][2][1]));
 }
 
 // PV phase.  Regions i = 0..31: MFMA i is O[t][ds] += V^T[cc][ds] P[t][cc]
 // with i = 2 (4 cc + ds) + t; V^T read r = 4 cc + ds (stream index 16 + r).
-// Pair ops [Q64_P1, 16) run in regions 0..21 (the last weight is written two
-// regions before the first cc = 3 MFMA), the row maxima of S_n in 22..31.
+// Regions 8 cc + 6 + t, after the last PV MFMA that reads P[t][cc], also add
+// that chunk's weights into the row sums ls[t].  Pair ops [Q64_P1, 16) run in
+// regions 0..21 (the last weight is written two regions before the first
+// cc = 3 MFMA), the row maxima of S_n in 22..31.
 template <bool HAS_NEXT>
 __device__ __forceinline__ void q64_pv(const char* vbase, const uint32_t (&voff)[4], f32x16 (&o)[2][4],
-                                       const f32x16 (&sc)[2][2], float c2, const float (&nm)[2], Q64Soft& sm,
-                                       float (&l)[2], const f32x16 (&sn)[2][2], float (&tmax)[2],
-                                       u32x4 (&op)[Q64_AHEAD + 1]) {
+                                       f32x4 (&ls)[2], const u32x4& sel, const f32x16 (&sc)[2][2], float c2,
+                                       const float (&nm)[2], Q64Soft& sm, const f32x16 (&sn)[2][2],
+                                       float (&tmax)[2], u32x4 (&op)[Q64_AHEAD + 1]) {
   constexpr int VROW = KS * 2;
-  constexpr int NOPS = (16 - Q64_P1) * 2 * 7;
+  constexpr int NOPS = (16 - Q64_P1) * 2 * Q64_PAIR_OPS;
   constexpr int NMAX = 2 * 17;
   float xm[2] = {-INFINITY, -INFINITY};
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     if (i < 22) {
 #pragma unroll
-      for (int q = (i * NOPS) / 22; q < ((i + 1) * NOPS) / 22; ++q) q64_pair_prog(sm, sc, Q64_P1, q, c2, nm, l);
+      for (int q = (i * NOPS) / 22; q < ((i + 1) * NOPS) / 22; ++q) q64_pair_prog(sm, sc, Q64_P1, q, c2, nm);
     } else if (HAS_NEXT) {
       const int j = i - 22;
 #pragma unroll
@@ -647,6 +658,7 @@ __device__ __forceinline__ void q64_pv(const char* vbase, const uint32_t (&voff)
     }
     const int t = i & 1, cc = r >> 2, ds = r & 3;
     mfma_o(o[t][ds], op[(16 + r) % (Q64_AHEAD + 1)], sm.pw[t][cc]);
+    if (ds == 3) mfma_l(ls[t], sel, sm.pw[t][cc]);
     fence();
   }
 }
@@ -664,13 +676,15 @@ __device__ __forceinline__ void q64_update(const float (&tmax)[2], float c2, flo
   }
 }
 
-// O *= corr for the tiles whose row maximum grew.  Written as asm (AGPR read,
-// multiply, AGPR write per register) so that no compiler-generated code
-// touches the AGPR accumulators inside the stage loop; the trailing s_nop
-// covers the AGPR write -> MFMA accumulator read of the next PV MFMA.
-__device__ __forceinline__ void agpr_scale(f32x16& o, float c) {
+// O *= corr and ls *= corr for the tiles whose reference maximum was raised.
+// Written as asm (AGPR read, multiply, AGPR write per register) so that no
+// compiler-generated code touches the AGPR accumulators inside the stage loop;
+// the trailing s_nop covers the AGPR write -> MFMA accumulator read of the
+// next PV MFMA.
+template <typename V, int N>
+__device__ __forceinline__ void agpr_scale(V& o, float c) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+  for (int r = 0; r < N; ++r) {
     float e = o[r], tmp;
     asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
                  : "+a"(e), "=&v"(tmp)
@@ -678,13 +692,15 @@ __device__ __forceinline__ void agpr_scale(f32x16& o, float c) {
     o[r] = e;
   }
 }
-__device__ __forceinline__ void q64_rescale(f32x16 (&o)[2][4], const float (&corr)[2], const bool (&any)[2]) {
+__device__ __forceinline__ void q64_rescale(f32x16 (&o)[2][4], f32x4 (&ls)[2], const float (&corr)[2],
+                                            const bool (&any)[2]) {
   fence();
 #pragma unroll
   for (int t = 0; t < 2; ++t)
     if (any[t]) {
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) agpr_scale(o[t][ds], corr[t]);
+      for (int ds = 0; ds < 4; ++ds) agpr_scale<f32x16, 16>(o[t][ds], corr[t]);
+      agpr_scale<f32x4, 4>(ls[t], corr[t]);
       asm volatile("s_nop 2" ::: "memory");
       fence();
     }
@@ -749,6 +765,13 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)lds);
   const uint32_t lds0w = lds0 + (uint32_t)w * 1024u;
+  // Row-sum selector, the A operand of mfma_l: 1.0 in every bf16 of lane l when
+  // bit 4 of l equals bit 2 of l, else 0 (A row l % 16, weight lane group l / 16).
+  // Made opaque once here, so that it stays in AGPRs instead of being rebuilt
+  // before each use.
+  const uint32_t sel_on = ((lane >> 4) & 1) == ((lane >> 2) & 1) ? 0x3F803F80u : 0u;
+  u32x4 sel = {sel_on, sel_on, sel_on, sel_on};
+  asm volatile("" : "+a"(sel));
 
   for (;;) {
     if (threadIdx.x == 0) item = atomicAdd(&counters[x], 1);
@@ -835,7 +858,12 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[t][i] = f32x16{};
-    float m[2] = {M_INIT, M_INIT}, l[2] = {0.f, 0.f}, corr[2] = {1.f, 1.f};
+    // Row sums: 16x16x32 accumulators whose lane l holds row l % 32 of its tile
+    // (the selector row of lane l is m = l % 16; it takes the weight operand's
+    // lane group g when g % 2 == (m / 4) % 2, i.e. the group holding the rows of
+    // the same parity half as the output rows m of lane group l / 16).
+    f32x4 ls[2] = {f32x4{}, f32x4{}};
+    float m[2] = {M_INIT, M_INIT}, corr[2] = {1.f, 1.f};
     bool any[2] = {false, false};
 
     int64_t pc = next_valid(t0);
@@ -892,34 +920,30 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
         // step A: current = (kb, 0) in sa, next = (kb, 1) -> sb
         bar_top();                      // K(kb, 1) landed
         issue_v(kb, 1, LV1);
-        l[0] *= corr[0];
-        l[1] *= corr[1];
         {
           const float nm[2] = {-m[0], -m[1]};
-          q64_qk<true>(kbuf1, vbuf0, koff, voff, qf, sb, sa, c2, nm, sm, l, op, [&]() {
+          q64_qk<true>(kbuf1, vbuf0, koff, voff, qf, sb, sa, c2, nm, sm, op, [&]() {
             bar_mid();                  // V(kb, 0) landed; every wave has read K(kb, 1)
             issue_k(kbn >= 0 ? kbn : kb, 1, LK1);
           });
-          q64_rescale(o, corr, any);
+          q64_rescale(o, ls, corr, any);
           if (kb == qb) q64_mask(sb, KS, qloc0, lane);
-          q64_pv<true>(vbuf0, voff, o, sa, c2, nm, sm, l, sb, tm, op);
+          q64_pv<true>(vbuf0, voff, o, ls, sel, sa, c2, nm, sm, sb, tm, op);
         }
         q64_update(tm, c2, m, corr, any);
 
         // step B: current = (kb, 1) in sb, next = (kbn, 0) -> sa
         bar_top();                      // K(kbn, 0) landed
         issue_v(kbn >= 0 ? kbn : kb, 0, LV0);
-        l[0] *= corr[0];
-        l[1] *= corr[1];
         {
           const float nm[2] = {-m[0], -m[1]};
-          q64_qk<true>(kbuf0, vbuf1, koff, voff, qf, sa, sb, c2, nm, sm, l, op, [&]() {
+          q64_qk<true>(kbuf0, vbuf1, koff, voff, qf, sa, sb, c2, nm, sm, op, [&]() {
             bar_mid();                  // V(kb, 1) landed; every wave has read K(kbn, 0)
             issue_k(kbnn >= 0 ? kbnn : kb, 0, LK0);
           });
-          q64_rescale(o, corr, any);
+          q64_rescale(o, ls, corr, any);
           if (kbn == qb) q64_mask(sa, 0, qloc0, lane);
-          q64_pv<true>(vbuf1, voff, o, sb, c2, nm, sm, l, sa, tm, op);
+          q64_pv<true>(vbuf1, voff, o, ls, sel, sb, c2, nm, sm, sa, tm, op);
         }
         if (kbn < 0) break;
         q64_update(tm, c2, m, corr, any);
@@ -934,7 +958,7 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float lt = halves_sum(l[t]);
+      const float lt = ls[t][0];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const size_t orow = (size_t)bh * n + (size_t)qb * BLK + qloc0 + 32 * t;
 #pragma unroll
