@@ -366,7 +366,7 @@ def model_sweep(args):
 def crossover(args):
     """Sparse layer (route + select + attention) vs dense attention over n."""
     rows = []
-    for n in (4096, 8192, 10240, 12288, 14336, 16384, 32768, 65536, 131072):
+    for n in (4096, 5120, 6144, 7168, 8192, 10240, 12288, 16384, 32768, 65536, 131072):
         layer = Layer(crossover_workload(n))
         res = layer.measure(1.0, max(args.steps, 5), max(args.warmup, 2))
         dense_ms, _ = layer.dense(max(args.dense_steps, 5))

@@ -218,13 +218,13 @@ int flex_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf
                 void* stream);
 
 /* Sequence length below which the sparse path does not pay for itself.
- * Routing and selection cost a fixed ~0.4 ms and a short causal map has few
- * tiles to skip, so dense attention wins on short inputs (the digest's
- * limitations paragraph, item 7, reports the same, with the crossover between
- * 8K and 64K tokens on its GPU).  Measured on one MI355X with Llama-shaped
- * layers (32 query / 8 KV heads, d = 128, 75% VS heads): dense / sparse layer
- * time 0.87 at n = 8192 and 1.12 at n = 10240. */
-#define CRISP_DENSE_BELOW_TOKENS 10240
+ * Routing and selection cost a near-fixed ~0.13 ms below 16K tokens and a
+ * short causal map has few tiles to skip, so dense attention wins on short
+ * inputs (the digest's limitations paragraph, item 7, reports the same, with
+ * the crossover between 8K and 64K tokens on its GPU).  Measured on one
+ * MI355X with Llama-shaped layers (32 query / 8 KV heads, d = 128, 75% VS
+ * heads): dense / sparse layer time 0.98 at n = 6144 and 1.15 at n = 7168. */
+#define CRISP_DENSE_BELOW_TOKENS 7168
 
 /* Which path a prefill of this shape takes: *use_dense = 1 when
  * shape->n < CRISP_DENSE_BELOW_TOKENS (call dense_attn), else 0 (call

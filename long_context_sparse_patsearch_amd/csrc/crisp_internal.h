@@ -31,7 +31,6 @@ struct SelectWs {
   float* kbar;          // [batch*h_kv][nb][d]
   float* abar;          // [bh][tri]  scaled logits, then x = A_bar / nb
   unsigned long long* hist_mass;  // [bh][2048]
-  uint32_t* hist_cnt;   // [bh][2048]
   unsigned long long* pe_state;   // [bh][8]
   int64_t* rowcnt;      // [rows]
   int32_t* eqcnt;       // [rows]

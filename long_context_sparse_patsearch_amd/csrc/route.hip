@@ -90,9 +90,12 @@ __global__ __launch_bounds__(BLK) void proxy_combine_kernel(const float* __restr
   const int64_t bh = blockIdx.x;
   const int i = threadIdx.x;
   const float* p = part + (size_t)bh * nchunks * BLK * 2 + (size_t)i * 2;
+  // unrolled so that the chunks' loads are in flight together (same order of operations)
   float M = -INFINITY;
+#pragma unroll 16
   for (int c = 0; c < nchunks; ++c) M = fmaxf(M, p[(size_t)c * BLK * 2]);
   float L = 0.f;
+#pragma unroll 16
   for (int c = 0; c < nchunks; ++c) L += p[(size_t)c * BLK * 2 + 1] * fast_exp2(p[(size_t)c * BLK * 2] - M);
   stats[((size_t)bh * BLK + i) * 2] = M;
   stats[((size_t)bh * BLK + i) * 2 + 1] = 1.f / L;

@@ -71,6 +71,7 @@ __device__ __forceinline__ int block_count(int v, int* red) {
 // kmin (top-k, ties to the lower index), then add the anchors 0 and N_b-1.
 // ------------------------------------------------------------------------------------------------
 constexpr int MAX_NB = 8192;   // n <= 1,048,576 tokens
+constexpr int RANK_NB = 1024;  // up to this many blocks the top-k fallback ranks every block at once
 
 __global__ __launch_bounds__(NTHR) void vs_select_kernel(
     const int8_t* __restrict__ pattern, const float* __restrict__ p_vert, const float* __restrict__ p_slash,
@@ -79,6 +80,7 @@ __global__ __launch_bounds__(NTHR) void vs_select_kernel(
   __shared__ float fv[4];
   __shared__ int fi[4];
   __shared__ uint8_t fl[MAX_NB];
+  __shared__ float pv[RANK_NB];
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
   const bool vs = pattern[bh] == 1;
@@ -105,6 +107,20 @@ __global__ __launch_bounds__(NTHR) void vs_select_kernel(
       for (int j = tid; j < nb; j += NTHR) fl[j] = (p[j] > thr) ? 1 : 0;
     } else if (kk == nb) {
       for (int j = tid; j < nb; j += NTHR) fl[j] = 1;
+    } else if (nb <= RANK_NB) {
+      // fewer than kmin blocks above the floor: the kk blocks first in the order (score
+      // descending, index ascending), i.e. those with fewer than kk blocks before them
+      for (int j = tid; j < nb; j += NTHR) pv[j] = p[j];
+      __syncthreads();
+      for (int j = tid; j < nb; j += NTHR) {
+        const float x = pv[j];
+        int before = 0;
+        for (int i = 0; i < nb; ++i) {
+          const float y = pv[i];
+          before += (y > x || (y == x && i < j)) ? 1 : 0;
+        }
+        fl[j] = before < kk ? 1 : 0;
+      }
     } else {
       // fewer than kmin blocks above the floor: top-kmin by score, ties to the lower index
       for (int j = tid; j < nb; j += NTHR) fl[j] = 0;
@@ -286,9 +302,6 @@ __global__ __launch_bounds__(NTHR) void pe_softmax_kernel(const int8_t* __restri
 __global__ void zero_u64_kernel(u64* p, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
-__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
-}
 
 __global__ void pe_state_init_kernel(const int8_t* __restrict__ pattern, u64* __restrict__ state, int64_t bh_total,
                                      u64 need) {
@@ -312,9 +325,8 @@ constexpr int HIST_CHUNK = 65536;
 
 __global__ __launch_bounds__(NTHR) void pe_hist_kernel(const int8_t* __restrict__ pattern, const float* __restrict__ abar,
                                                        const u64* __restrict__ state, u64* __restrict__ hmass,
-                                                       uint32_t* __restrict__ hcnt, int64_t tri, int pass) {
+                                                       int64_t tri, int pass) {
   __shared__ u64 lm[HBINS];
-  __shared__ uint32_t lc[HBINS];
   const int64_t bh = blockIdx.y;
   if (pattern[bh] != 0) return;
   const u64* st = state + bh * ST_WORDS;
@@ -323,7 +335,7 @@ __global__ __launch_bounds__(NTHR) void pe_hist_kernel(const int8_t* __restrict_
   pass_bits(pass, shift, width);
   const int pshift = shift + width;                  // bits above this pass's digit
   const uint32_t prefix = (uint32_t)st[ST_PREFIX];
-  for (int i = threadIdx.x; i < HBINS; i += NTHR) { lm[i] = 0; lc[i] = 0; }
+  for (int i = threadIdx.x; i < HBINS; i += NTHR) lm[i] = 0;
   __syncthreads();
   const uint32_t* keys = reinterpret_cast<const uint32_t*>(abar + (size_t)bh * tri);
   const int64_t e0 = (int64_t)blockIdx.x * HIST_CHUNK;
@@ -334,44 +346,81 @@ __global__ __launch_bounds__(NTHR) void pe_hist_kernel(const int8_t* __restrict_
     if (pass > 0 && (key >> pshift) != prefix) continue;
     const uint32_t dig = (key >> shift) & dmask;
     atomicAdd(&lm[dig], mass_fx(key));
-    atomicAdd(&lc[dig], 1u);
   }
   __syncthreads();
   u64* gm = hmass + bh * HBINS;
-  uint32_t* gc = hcnt + bh * HBINS;
   for (int i = threadIdx.x; i < HBINS; i += NTHR)
-    if (lc[i]) {
-      atomicAdd(&gm[i], lm[i]);
-      atomicAdd(&gc[i], lc[i]);
-    }
+    if (lm[i]) atomicAdd(&gm[i], lm[i]);
 }
 
-__global__ __launch_bounds__(NTHR) void pe_find_kernel(const int8_t* __restrict__ pattern, const u64* __restrict__ hmass,
-                                                       const uint32_t* __restrict__ hcnt, u64* __restrict__ state, int pass) {
+// Run by one full wave: the first bucket, from the top (nbk - 1) down, at which the running mass
+// reaches rem.  Lane j sums its buckets nbk-1-per*j down to nbk-per*(j+1) (per = nbk / 64),
+// starting at a lane-rotated offset so that the wave's LDS reads fall in distinct banks; an
+// inclusive prefix over the lanes finds the lane that crosses rem, and that lane walks its own
+// buckets.  Returns false on every lane when all buckets together stay below rem; otherwise lane
+// `owner` gets the bucket (`found`) and the mass of the buckets above it (`above`).  The same
+// bucket and mass as a walk from the top over all buckets: the sums are exact integers.
+__device__ __forceinline__ bool wave_bucket_search(const u64* lm, int nbk, u64 rem, int lane, int& owner, int& found,
+                                                   u64& above) {
+  const int per = nbk / 64, top = nbk - 1 - per * lane;
+  u64 own = 0;
+  for (int i = 0; i < per; ++i) own += lm[top - (i + lane) % per];
+  u64 incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const u64 v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  const u64 hit = __ballot(incl >= rem);
+  if (hit == 0) return false;
+  owner = __builtin_ctzll(hit);
+  if (lane == owner) {
+    u64 cum = incl - own;
+    int f = top - per + 1;
+    for (int i = 0; i < per; ++i) {
+      if (cum + lm[top - i] >= rem) {
+        f = top - i;
+        break;
+      }
+      cum += lm[top - i];
+    }
+    found = f;
+    above = cum;
+  }
+  return true;
+}
+
+// Reads the head's histogram of this pass and clears it for the next one (a head whose
+// histogram is never filled again, VS or already decided, keeps a cleared one).
+__global__ __launch_bounds__(NTHR) void pe_find_kernel(const int8_t* __restrict__ pattern, u64* __restrict__ hmass,
+                                                       u64* __restrict__ state, int pass) {
   __shared__ u64 lm[HBINS];
   const int64_t bh = blockIdx.x;
   if (pattern[bh] != 0) return;
   u64* st = state + bh * ST_WORDS;
   if (st[ST_ALL]) return;
-  for (int i = threadIdx.x; i < HBINS; i += NTHR) lm[i] = hmass[bh * HBINS + i];
+  for (int i = threadIdx.x; i < HBINS; i += NTHR) {
+    lm[i] = hmass[bh * HBINS + i];
+    hmass[bh * HBINS + i] = 0;
+  }
   __syncthreads();
-  if (threadIdx.x != 0) return;
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
   int shift, width;
   pass_bits(pass, shift, width);
   const u64 need = st[ST_NEED] - st[ST_ABOVE];
+  int owner = 0, found = 0;
   u64 cum = 0;
-  int found = -1;
-  for (int bkt = (1 << width) - 1; bkt >= 0; --bkt) {
-    if (cum + lm[bkt] >= need) { found = bkt; break; }
-    cum += lm[bkt];
-  }
-  if (found < 0) {
+  if (!wave_bucket_search(lm, 1 << width, need, lane, owner, found, cum)) {
     // the whole map sums to less than gamma: keep every cell
-    st[ST_ALL] = 1;
-    st[ST_T] = 0;
-    st[ST_TAKE] = ~0ull;
+    if (lane == 0) {
+      st[ST_ALL] = 1;
+      st[ST_T] = 0;
+      st[ST_TAKE] = ~0ull;
+    }
     return;
   }
+  if (lane != owner) return;
   st[ST_PREFIX] = (st[ST_PREFIX] << width) | (u64)found;
   st[ST_ABOVE] += cum;
   if (pass == 2) {
@@ -380,7 +429,6 @@ __global__ __launch_bounds__(NTHR) void pe_find_kernel(const int8_t* __restrict_
     const u64 rem = st[ST_NEED] - st[ST_ABOVE];
     const u64 mt = mass_fx(T);
     st[ST_TAKE] = mt ? (rem + mt - 1) / mt : ~0ull;
-    (void)hcnt;
   }
 }
 
@@ -418,33 +466,13 @@ __global__ __launch_bounds__(NTHR) void pe_row_select_kernel(const int8_t* __res
     }
     __syncthreads();
     if (tid < 64) {
-      // buckets from the top: lane j owns buckets nbk-1-32j .. nbk-32-32j (nbk = 2^width <= 2048)
-      const int nbk = 1 << width, per = nbk / 64;
-      const u64 rem = need - sh[1];
-      u64 own = 0;
-      for (int i = 0; i < per; ++i) own += lm[nbk - 1 - per * lane - i];
-      u64 incl = own;   // inclusive prefix over lanes (top buckets first)
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const u64 v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
-      }
-      const u64 hit = __ballot(incl >= rem);
-      if (hit == 0) {
+      int owner = 0, found = 0;
+      u64 cum = 0;
+      if (!wave_bucket_search(lm, 1 << width, need - sh[1], lane, owner, found, cum)) {
         if (lane == 0) sh[2] = 1;   // the row sums to less than gamma: keep it all
-      } else {
-        const int j = __builtin_ctzll(hit);
-        if (lane == j) {
-          u64 cum = incl - own;
-          int found = nbk - 1 - per * lane;
-          for (int i = 0; i < per; ++i) {
-            const int bkt = nbk - 1 - per * lane - i;
-            if (cum + lm[bkt] >= rem) { found = bkt; break; }
-            cum += lm[bkt];
-          }
-          sh[0] = (sh[0] << width) | (u64)found;
-          sh[1] += cum;
-        }
+      } else if (lane == owner) {
+        sh[0] = (sh[0] << width) | (u64)found;
+        sh[1] += cum;
       }
     }
     __syncthreads();
@@ -699,12 +727,10 @@ hipError_t select_impl(const Dims& dm, float alpha, float gamma, int kmin, const
     const u64 need = (u64)ceil((double)gamma * 0x1p60);
     pe_state_init_kernel<<<(bh + 255) / 256, 256, 0, st>>>(pattern, ws.pe_state, dm.bh, need);
     const unsigned hchunks = (unsigned)((dm.tri + HIST_CHUNK - 1) / HIST_CHUNK);
+    zero_u64_kernel<<<256, 256, 0, st>>>(ws.hist_mass, dm.bh * HBINS);   // later passes: cleared by pe_find
     for (int pass = 0; pass < 3; ++pass) {
-      zero_u64_kernel<<<256, 256, 0, st>>>(ws.hist_mass, dm.bh * HBINS);
-      zero_u32_kernel<<<256, 256, 0, st>>>(ws.hist_cnt, dm.bh * HBINS);
-      pe_hist_kernel<<<dim3(hchunks, bh), NTHR, 0, st>>>(pattern, ws.abar, ws.pe_state, ws.hist_mass, ws.hist_cnt, dm.tri,
-                                                         pass);
-      pe_find_kernel<<<bh, NTHR, 0, st>>>(pattern, ws.hist_mass, ws.hist_cnt, ws.pe_state, pass);
+      pe_hist_kernel<<<dim3(hchunks, bh), NTHR, 0, st>>>(pattern, ws.abar, ws.pe_state, ws.hist_mass, dm.tri, pass);
+      pe_find_kernel<<<bh, NTHR, 0, st>>>(pattern, ws.hist_mass, ws.pe_state, pass);
     }
     row_count_kernel<<<(unsigned)dm.rows, 64, 0, st>>>(pattern, ws.vsflags, ws.abar, ws.pe_state, ws.rowcnt, ws.eqcnt,
                                                         ws.seltake, nb, dm.tri, band, nullptr);
@@ -736,7 +762,6 @@ size_t select_ws_layout(const Dims& dm, SelectWs* ws, char* base) {
   w.kbar = (float*)take((size_t)dm.batch * dm.h_kv * dm.nb * dm.d * 4);
   w.abar = (float*)take((size_t)dm.bh * dm.tri * 4);
   w.hist_mass = (unsigned long long*)take((size_t)dm.bh * HBINS * 8);
-  w.hist_cnt = (uint32_t*)take((size_t)dm.bh * HBINS * 4);
   w.pe_state = (unsigned long long*)take((size_t)dm.bh * ST_WORDS * 8);
   w.rowcnt = (int64_t*)take((size_t)dm.rows * 8);
   w.eqcnt = (int32_t*)take((size_t)dm.rows * 4);

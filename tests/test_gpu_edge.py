@@ -3,6 +3,9 @@
 Every case goes through the C-ABI library and is compared with the fp64 oracle
 on the same seeded inputs (prefill_inputs), under the rules of parity.py.
 """
+import os
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -103,6 +106,8 @@ CASES = [
     ("gqa7_nb16", dict(k_min_tokens=2048)),
     ("mha_nb32_d64", dict(gamma=1.0)),
     ("mha_nb32_d64", dict(gamma=0.5, tau=0.05)),
+    ("mha_nb32_d64", dict(alpha=3.0, k_min_tokens=1536)),
+    ("ragged_nb9_b2_g2", dict(alpha=3.0, k_min_tokens=768)),
 ]
 
 
@@ -186,7 +191,11 @@ def test_empty_batch_is_a_no_op():
     assert r["pattern"].numel() == 0 and o.numel() == 0 and d.numel() == 0 and s["row_ptr"].numel() == 1
 
 
-@pytest.mark.parametrize("n", [4096, 10240])
+_HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "crisp.h")
+_GATE = int(re.search(r"#define\s+CRISP_DENSE_BELOW_TOKENS\s+(\d+)", open(_HEADER).read()).group(1))
+
+
+@pytest.mark.parametrize("n", [4096, _GATE - 128, _GATE])
 def test_prefill_length_gate(n):
     """prefill() runs dense attention below the library's crossover length and
     the sparse path from it on; either way the output is exactly what the
@@ -195,7 +204,7 @@ def test_prefill_length_gate(n):
     q, k, v = device_inputs(_inputs(sh, seed=61))
     cfg = crisp.config()
     res = crisp.prefill(q, k, v, cfg)
-    want_dense = n < 10240
+    want_dense = n < _GATE
     assert crisp.use_dense(crisp.shape_of(q, k)) is want_dense
     assert res["path"] == ("dense" if want_dense else "sparse")
     if want_dense:
