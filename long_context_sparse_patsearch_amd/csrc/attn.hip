@@ -571,10 +571,32 @@ __device__ __forceinline__ void q64_pair_op(Q64Soft& sm, const f32x16 (&sc)[2][2
     default: sm.pw[t][p >> 2][p & 3] = pack_bf16x2(sm.a0[t][p], sm.a1[t][p]);
   }
 }
-// op q of the pair program over pairs [p0, p0 + np) of both tiles (pair-major, tiles alternating)
+// op q of the pair program over NP pairs from p0 of both tiles (pair-major, tiles
+// alternating).  Each pair's pack is deferred into the next pair, between its two exp2: pair 0
+// runs FMA, FMA, exp2, exp2; pair pp >= 1 runs FMA, FMA, exp2, pack of pair pp - 1, exp2; the
+// last op packs pair NP - 1.  A pack issued right behind the exp2 it reads stalls the wave
+// (and the next MFMA) on the transcendental's latency, and this order also spreads the exp2s
+// evenly over the regions (about 16 VALU cycles per region, what one MFMA leaves free).
+template <int NP>
 __device__ __forceinline__ void q64_pair_prog(Q64Soft& sm, const f32x16 (&sc)[2][2], int p0, int q, float c2,
                                               const float (&nm)[2]) {
-  const int pp = q / Q64_PAIR_OPS, k = q % Q64_PAIR_OPS;
+  int pp, k;
+  if (q < 4) {
+    pp = 0;
+    k = q;
+  } else if (q == Q64_PAIR_OPS * NP - 1) {
+    pp = NP - 1;
+    k = 4;
+  } else {
+    const int r = q - 4, slot = r % Q64_PAIR_OPS;
+    pp = 1 + r / Q64_PAIR_OPS;
+    if (slot == 3) {
+      pp -= 1;
+      k = 4;
+    } else {
+      k = slot < 3 ? slot : 3;
+    }
+  }
   q64_pair_op(sm, sc, pp & 1, p0 + (pp >> 1), k, c2, nm);
 }
 
@@ -600,7 +622,7 @@ __device__ __forceinline__ void q64_qk(const char* kbase, const char* vbase, con
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
 #pragma unroll
-    for (int q = (i * NOPS) / 32; q < ((i + 1) * NOPS) / 32; ++q) q64_pair_prog(sm, sc, 0, q, c2, nm);
+    for (int q = (i * NOPS) / 32; q < ((i + 1) * NOPS) / 32; ++q) q64_pair_prog<Q64_P1 * 2>(sm, sc, 0, q, c2, nm);
     const int r = i >> 1;
     // the stage's K reads are all issued; the mid-step barrier comes before the first V^T read
     if (i == 2 * (16 - Q64_AHEAD)) mid();
@@ -637,7 +659,8 @@ __device__ __forceinline__ void q64_pv(const char* vbase, const uint32_t (&voff)
   for (int i = 0; i < 32; ++i) {
     if (i < 22) {
 #pragma unroll
-      for (int q = (i * NOPS) / 22; q < ((i + 1) * NOPS) / 22; ++q) q64_pair_prog(sm, sc, Q64_P1, q, c2, nm);
+      for (int q = (i * NOPS) / 22; q < ((i + 1) * NOPS) / 22; ++q)
+        q64_pair_prog<(16 - Q64_P1) * 2>(sm, sc, Q64_P1, q, c2, nm);
     } else if (HAS_NEXT) {
       const int j = i - 22;
 #pragma unroll
