@@ -521,9 +521,9 @@ __device__ __forceinline__ void mfma_o(f32x16& o, const u32x4& a, const u32x4& b
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
 // ls += SEL W: row sums of one 16-key chunk of weights (W, the B operand of the
-// PV MFMAs), ls and the selector in AGPRs
+// PV MFMAs), ls in VGPRs, the selector in AGPRs
 __device__ __forceinline__ void mfma_l(f32x4& ls, const u32x4& sel, const u32x4& w) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(ls) : "a"(sel), "v"(w));
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(ls) : "a"(sel), "v"(w));
 }
 // 13 wait states: covers an MFMA result read by VALU code (or its accumulator
 // overwritten by VALU code) right after the MFMA
@@ -700,10 +700,11 @@ __device__ __forceinline__ void q64_update(const float (&tmax)[2], float c2, flo
 }
 
 // O *= corr and ls *= corr for the tiles whose reference maximum was raised.
-// Written as asm (AGPR read, multiply, AGPR write per register) so that no
+// O is scaled in asm (AGPR read, multiply, AGPR write per register) so that no
 // compiler-generated code touches the AGPR accumulators inside the stage loop;
 // the trailing s_nop covers the AGPR write -> MFMA accumulator read of the
-// next PV MFMA.
+// next PV MFMA.  The row sums are VGPRs, scaled by plain multiplies (their next
+// MFMA is regions away).
 template <typename V, int N>
 __device__ __forceinline__ void agpr_scale(V& o, float c) {
 #pragma unroll
@@ -723,7 +724,7 @@ __device__ __forceinline__ void q64_rescale(f32x16 (&o)[2][4], f32x4 (&ls)[2], c
     if (any[t]) {
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) agpr_scale<f32x16, 16>(o[t][ds], corr[t]);
-      agpr_scale<f32x4, 4>(ls[t], corr[t]);
+      ls[t] *= corr[t];
       asm volatile("s_nop 2" ::: "memory");
       fence();
     }
