@@ -484,20 +484,23 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void attn_kernel(
 // and the Q operands (touched only by MFMAs) in AGPRs, so the MFMAs are
 // issued as inline asm and the schedule is written out in regions fenced
 // with sched_barrier: each region holds a slice of the softmax VALU work, at
-// most one operand read, and one MFMA.  The softmax of a stage is split
+// most one operand read, and one MFMA (two where a row-sum MFMA follows a PV
+// MFMA).  The softmax of a stage is split
 // between the QK phase (weight pairs [0, Q64_P1) of each tile) and the PV
 // phase (the rest, done by the time the PV MFMAs need them, then the next
 // stage's row maxima).  The row sums come from the matrix cores as well: after
 // the PV MFMAs of a 16-key chunk, one 16x16x32 MFMA multiplies a constant 0/1
 // selector with that chunk's weight operand, which adds the chunk's bf16
-// weights of each query row into a 4-register accumulator in that row's lanes.
+// weights of each query row into a 4-register accumulator (VGPRs) in that
+// row's lanes.
 //
 // The compiler does not see the MFMAs inside the asm, so the wait states the
 // hardware needs around them are kept by construction: a weight pair is
 // written at least two regions before the PV MFMA that reads it (VALU write
-// -> MFMA read needs 2), the scores are read by VALU code only in later
-// regions or after an explicit s_nop (MFMA write -> VALU read needs 12), and
-// the output rescale ends with an s_nop (AGPR write -> MFMA read needs 2).
+// -> MFMA read needs 2), the scores and row sums are read or rescaled by VALU
+// code only in later regions or after an explicit s_nop (MFMA write -> VALU
+// read needs 12), and the output rescale ends with an s_nop (AGPR write ->
+// MFMA read needs 2).  tests/test_isa_hazards.py checks the compiled kernel.
 // ---------------------------------------------------------------------------
 constexpr int Q64_THR = 128;       // two waves: one 128-row query block per workgroup
 constexpr int Q64_WG_PER_CU = 2;   // four waves per CU, one per SIMD
