@@ -151,7 +151,9 @@ int crisp_select(const crisp_shape* shape, const crisp_cfg* cfg,
  * outside [0, qb] are skipped).  A query with no visible key gets output 0.
  * out: [batch][h_q][n][d], f32 (CRISP_OUT_F32) or bf16 (CRISP_OUT_BF16).
  * bf16 MFMA for QK^T and PV with fp32 accumulation; softmax in fp32 with P
- * rounded to bf16 for the PV product.
+ * rounded to bf16 for the PV product and the row sums taken over those same
+ * rounded weights; a row's softmax reference maximum is raised only when a
+ * stage's maximum exceeds it by more than 2^8 (the normalisation cancels it).
  * ws: crisp_workspace_bytes(CRISP_CALL_ATTN) bytes (work-queue counters; the
  * call resets them, so concurrent calls must not share one workspace). */
 int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg,
