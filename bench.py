@@ -62,6 +62,14 @@ def parse():
     return ap.parse_args()
 
 
+def attn_source_sha256():
+    """Digest of the attention kernel's source: HBM counters taken on another version are not reported."""
+    import hashlib
+    path = os.path.join(ROOT, "long_context_sparse_patsearch_amd", "csrc", "attn.hip")
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
 def _event():
     import torch
     return torch.cuda.Event(enable_timing=True)
@@ -473,7 +481,8 @@ def main():
     if args.traffic and os.path.exists(args.traffic):
         with open(args.traffic) as fh:
             tr = json.load(fh)
-        if tr.get("workload") == res["workload"] and tr.get("alpha") == alpha and tr.get("tiles") == res["tiles"]:
+        if (tr.get("workload") == res["workload"] and tr.get("alpha") == alpha and tr.get("tiles") == res["tiles"]
+                and tr.get("attn_source_sha256") == attn_source_sha256()):
             traffic = tr.get("bytes_per_launch")
     tflops = res["attn_tflops"]
     out = {
