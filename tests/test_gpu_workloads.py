@@ -54,6 +54,14 @@ def test_layer_parity(idx, alpha):
     _log(f"[{wl.name} alpha={alpha}] gpu layer")
     g = gpu_layer(q, k, v, cfg)
     check_csr_structure(g, sh.batch * sh.h_q, nb, crisp.max_blocks(crisp.shape_of(q, k)))
+    # every (head, query block) item of the attention's work queues is run, and runs alike every time:
+    # a second launch into a NaN-filled buffer must write every element, with the first launch's bits
+    again = torch.full_like(g["out"], float("nan"))
+    crisp.sparse_attn(q, k, v, g["sel"], cfg, out=again)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(again).all()), "an output row was not written"
+    assert torch.equal(again, g["out"]), "a second launch gave other bits"
+    again = None
     _log(f"[{wl.name} alpha={alpha}] oracle selection")
     ora = oracle_layer(inp, ckw)
     ora, stats = check_selection(g, inp, ora, ckw, sh.h_q, nb)
@@ -75,8 +83,9 @@ def test_layer_parity(idx, alpha):
     worst, mean = check_outputs(g["out"], inp, rows, blocks, q_rows=q_rows)
     _log(f"[{wl.name} alpha={alpha}] outputs ok: max-abs {worst:.2e} mean-abs {mean:.2e}")
     if alpha == wl.alphas[0]:
-        dense = crisp.dense_attn(q, k, v)
+        dense = crisp.dense_attn(q, k, v, out=torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device))
         torch.cuda.synchronize()
+        assert bool(torch.isfinite(dense).all()), "a dense output row was not written"
         drows = {bh: co.dense_rows(nb) for bh in ora}
         dblocks = {bh: (range(nb) if idx == 1 else sample_blocks(nb, rng, extra=0)) for bh in list(ora)[::max(1, sh.h_q // 8)]}
         worst, mean = check_outputs(dense, inp, drows, dblocks, q_rows=q_rows)
