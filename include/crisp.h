@@ -225,8 +225,8 @@ int flex_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf
  * inputs (the digest's limitations paragraph, item 7, reports the same, with
  * the crossover between 8K and 64K tokens on its GPU).  Measured on one
  * MI355X with Llama-shaped layers (32 query / 8 KV heads, d = 128, 75% VS
- * heads): dense / sparse layer time 0.94-0.98 at n = 6144 and 1.10-1.15 at
- * n = 7168 (two runs). */
+ * heads): dense / sparse layer time 0.93-0.98 at n = 6144 and 1.07-1.15 at
+ * n = 7168 (three runs). */
 #define CRISP_DENSE_BELOW_TOKENS 7168
 
 /* Which path a prefill of this shape takes: *use_dense = 1 when
