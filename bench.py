@@ -392,7 +392,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the method is per attention "
-              "head and this build runs one GPU's share of heads (the sharding plan is a design note only).",
+              "head and this library runs one GPU's share of heads (sharding across GPUs is not implemented).",
               file=sys.stderr)
         sys.exit(2)
     import torch

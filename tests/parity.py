@@ -1,6 +1,6 @@
-"""Helpers of the GPU parity tests: run the C-ABI path, judge it against the oracle.
+"""Helpers of the GPU parity tests: run the C-ABI path, check it against the oracle.
 
-Rules (all judged with the oracle's values):
+Rules (all decided with the oracle's values):
 * routing: the pattern must match unless |C_struct - tau| <= 1e-5 * tau; such a
   head is re-run in the oracle with the GPU's pattern forced.
 * VS selection: a block may differ only if its score is within 1e-5 relative of
