@@ -70,6 +70,19 @@ def attn_source_sha256():
         return hashlib.sha256(fh.read()).hexdigest()
 
 
+def measured_traffic(path, workload, alpha, tiles):
+    """HBM bytes per attention launch from the stored counter run, or None when that run
+    measured another workload, setting, tile count or attention source."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        tr = json.load(fh)
+    if (tr.get("workload") == workload and tr.get("alpha") == alpha and tr.get("tiles") == tiles
+            and tr.get("attn_source_sha256") == attn_source_sha256()):
+        return tr.get("bytes_per_launch")
+    return None
+
+
 def _event():
     import torch
     return torch.cuda.Event(enable_timing=True)
@@ -477,13 +490,7 @@ def main():
     dense_ms, dense_tf = dense.get(res["workload"], (None, None))
     also = [r for r in results if not r["_primary"]]
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as fh:
-            tr = json.load(fh)
-        if (tr.get("workload") == res["workload"] and tr.get("alpha") == alpha and tr.get("tiles") == res["tiles"]
-                and tr.get("attn_source_sha256") == attn_source_sha256()):
-            traffic = tr.get("bytes_per_launch")
+    traffic = measured_traffic(args.traffic, res["workload"], alpha, res["tiles"])
     tflops = res["attn_tflops"]
     out = {
         "metric": METRIC,
