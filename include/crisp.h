@@ -152,10 +152,16 @@ int crisp_select(const crisp_shape* shape, const crisp_cfg* cfg,
  * out: [batch][h_q][n][d], f32 (CRISP_OUT_F32) or bf16 (CRISP_OUT_BF16).
  * bf16 MFMA for QK^T and PV with fp32 accumulation; softmax in fp32 with P
  * rounded to bf16 for the PV product and the row sums taken over those same
- * rounded weights; a row's softmax reference maximum is raised only when a
- * stage's maximum exceeds it by more than 2^8 (the normalisation cancels it).
- * ws: crisp_workspace_bytes(CRISP_CALL_ATTN) bytes (work-queue counters; the
- * call resets them, so concurrent calls must not share one workspace). */
+ * rounded weights, so the choice of each row's softmax reference maximum m
+ * cancels in the normalisation.  At d = 128, m is the maximum of the row's
+ * first 64 keys whenever the Cauchy-Schwarz bound of every logit of the row
+ * (|q| times the largest key norm of its KV head, over sqrt(d)) lies at most
+ * 64 log2 units above it (weights then stay below 2^64); otherwise, and at
+ * d = 64, m is raised whenever a 64-key stage's maximum exceeds it by more
+ * than 2^8.
+ * ws: crisp_workspace_bytes(CRISP_CALL_ATTN) bytes (work-queue counters, the
+ * largest key norm of each KV head and a V^T copy of V; the call resets them,
+ * so concurrent calls must not share one workspace). */
 int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg,
                       const void* q_bf16, const void* k_bf16, const void* v_bf16,
                       const int64_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
@@ -164,8 +170,8 @@ int crisp_sparse_attn(const crisp_shape* shape, const crisp_cfg* cfg,
 /* Dense exact causal attention (the result FlashAttention computes; digest,
  * prerequisite section on FlashAttention): crisp_sparse_attn with every key
  * block kb <= qb selected, same kernels and precision.
- * ws: crisp_workspace_bytes(CRISP_CALL_DENSE) bytes (work-queue counters and
- * a V^T copy of V, as for crisp_sparse_attn). */
+ * ws: crisp_workspace_bytes(CRISP_CALL_DENSE) bytes (as for
+ * crisp_sparse_attn). */
 int dense_attn(const crisp_shape* shape, const void* q_bf16, const void* k_bf16,
                const void* v_bf16, void* out, int out_dtype, void* ws, size_t ws_bytes,
                void* stream);

@@ -25,6 +25,8 @@
 // MFMAs.
 #include <math.h>
 
+#include <type_traits>
+
 #include "crisp_device.hpp"
 #include "crisp_internal.h"
 
@@ -563,6 +565,19 @@ __device__ __forceinline__ float halves_max(float t) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// sum over lanes l and l ^ 32, added in the same order in both lanes
+__device__ __forceinline__ float halves_sum(float t) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A row keeps the first stage's maximum as its fixed reference when its
+// Cauchy-Schwarz logit bound c2 |q| max|k| (times BOUND_SLACK, which covers
+// the rounding of the norms and of the fp32 dot products) lies at most
+// FIXED_SPAN (log2 units) above it: weights then stay <= 2^FIXED_SPAN and a
+// row sum over up to 2^20 keys far below the fp32 range.
+constexpr float FIXED_SPAN = 64.f;
+constexpr float BOUND_SLACK = 1.f + 1.f / 256.f;
 
 // Softmax state of one stage for both tiles.  Weight pair p of tile t covers
 // accumulator registers 2p, 2p+1 (ks = p / 8) and becomes 32-bit word p % 4 of
@@ -661,7 +676,7 @@ __device__ __forceinline__ void q64_qk(const char* kbase, const char* vbase, con
 // that chunk's weights into the row sums ls[t].  Pair ops [Q64_P1, 16) run in
 // regions 0..21 (the last weight is written two regions before the first
 // cc = 3 MFMA), the row maxima of S_n in 22..31.
-template <bool HAS_NEXT>
+template <bool HAS_NEXT, bool TRACK_MAX = true>
 __device__ __forceinline__ void q64_pv(const char* vbase, const uint32_t (&voff)[4], f32x16 (&o)[2][4],
                                        f32x4 (&ls)[2], const u32x4& sel, const f32x16 (&sc)[2][2], float c2,
                                        const float (&nm)[2], Q64Soft& sm, const f32x16 (&sn)[2][2],
@@ -676,7 +691,7 @@ __device__ __forceinline__ void q64_pv(const char* vbase, const uint32_t (&voff)
 #pragma unroll
       for (int q = (i * NOPS) / 22; q < ((i + 1) * NOPS) / 22; ++q)
         q64_pair_prog<(16 - Q64_P1) * 2>(sm, sc, Q64_P1, q, c2, nm);
-    } else if (HAS_NEXT) {
+    } else if (HAS_NEXT && TRACK_MAX) {
       const int j = i - 22;
 #pragma unroll
       for (int q = (j * NMAX) / 10; q < ((j + 1) * NMAX) / 10; ++q) {
@@ -745,6 +760,19 @@ __device__ __forceinline__ void q64_rescale(f32x16 (&o)[2][4], f32x4 (&ls)[2], c
     }
 }
 
+// Row maxima (score units) of a stage's scores, both lanes of a query column.
+__device__ __forceinline__ void q64_rowmax(const f32x16 (&s)[2][2], float (&tm)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float xm = -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) xm = fmaxf(fmaxf(xm, s[t][ks][r]), s[t][ks][r + 1]);
+    tm[t] = halves_max(xm);
+  }
+}
+
 __device__ __forceinline__ void q64_mask(f32x16 (&s)[2][2], int kloc0, int qloc0, int lane) {
   mfma_drain();
   mask_diag(s[0], kloc0, qloc0, lane);
@@ -756,7 +784,8 @@ template <bool DENSE, bool OUT_BF16>
 __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_q64_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
     const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_cap,
-    void* __restrict__ out, int n, int h_q, int group, Queue qd, int* __restrict__ counters, float c2) {
+    void* __restrict__ out, int n, int h_q, int group, Queue qd, int* __restrict__ counters,
+    const float* __restrict__ kn2max, float c2) {
   constexpr int D = 128;
   using S = Stage<D>;
   // LDS: K stage buffers 0 and 1, then V^T stage buffers 0 and 1 (as in attn_kernel)
@@ -897,6 +926,28 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #pragma unroll
       for (int s = 0; s < S::NSTEP; ++s) qf[t][s] = *reinterpret_cast<const u32x4*>(qp + 16 * s);
     }
+    // Squared norm of each of the wave's query rows (both lanes of a row hold
+    // it), from a second read of the rows through an address the compiler
+    // cannot match with qf's: read from qf, the operands would stay in VGPRs
+    // and move to their AGPRs right before the first MFMAs, one instruction
+    // short of the wait the hardware needs there.
+    float qn2[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* qp = q + ((size_t)bh * n + (size_t)qb * BLK + qloc0 + 32 * t) * D + 8 * hi;
+      asm volatile("" : "+v"(qp));
+      float acc = 0.f;
+#pragma unroll
+      for (int s = 0; s < S::NSTEP; ++s) {
+        const u32x4 x4 = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 x = __builtin_bit_cast(bf16x2, x4[e]);
+          acc = __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
+        }
+      }
+      qn2[t] = halves_sum(acc);
+    }
     f32x16 o[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -960,6 +1011,25 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
         tm[t] = halves_max(xm);
       }
       q64_update(tm, c2, m, corr, any);
+      // Fixed reference maximum.  When every logit of the wave's rows is provably
+      // at most FIXED_SPAN above the first stage's maximum m (Cauchy-Schwarz:
+      // s <= |q| max|k|), m stays for the whole row: no stage needs its maximum,
+      // a rescale test or a rescale, and the weights stay below 2^FIXED_SPAN.
+      // Otherwise (a loose bound) the wave tracks its rows' maxima stage by stage
+      // in a block after each step's PV phase.  Both cases run the same loop (a
+      // second copy of it makes the register allocator spill).
+      bool track;
+      {
+        const float kn2 = kn2max[(size_t)b * h_kv + g];
+        bool loose = false;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float bound = c2 * __builtin_sqrtf(qn2[t] * kn2) * BOUND_SLACK;
+          loose |= !(bound - m[t] <= FIXED_SPAN);
+        }
+        track = __ballot(loose) != 0;
+        if (!track) any[0] = any[1] = false;
+      }
       for (;;) {
         // step A: current = (kb, 0) in sa, next = (kb, 1) -> sb
         bar_top();                      // K(kb, 1) landed
@@ -972,9 +1042,12 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
           });
           q64_rescale(o, ls, corr, any);
           if (kb == qb) q64_mask(sb, KS, qloc0, lane);
-          q64_pv<true>(vbuf0, voff, o, ls, sel, sa, c2, nm, sm, sb, tm, op);
+          q64_pv<true, false>(vbuf0, voff, o, ls, sel, sa, c2, nm, sm, sb, tm, op);
         }
-        q64_update(tm, c2, m, corr, any);
+        if (track) {
+          q64_rowmax(sb, tm);
+          q64_update(tm, c2, m, corr, any);
+        }
 
         // step B: current = (kb, 1) in sb, next = (kbn, 0) -> sa
         bar_top();                      // K(kbn, 0) landed
@@ -987,10 +1060,13 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
           });
           q64_rescale(o, ls, corr, any);
           if (kbn == qb) q64_mask(sa, 0, qloc0, lane);
-          q64_pv<true>(vbuf1, voff, o, ls, sel, sb, c2, nm, sm, sa, tm, op);
+          q64_pv<true, false>(vbuf1, voff, o, ls, sel, sb, c2, nm, sm, sa, tm, op);
         }
         if (kbn < 0) break;
-        q64_update(tm, c2, m, corr, any);
+        if (track) {
+          q64_rowmax(sa, tm);
+          q64_update(tm, c2, m, corr, any);
+        }
         kb = kbn;
         pn = pnn;
         kbn = kbnn;
@@ -1025,10 +1101,13 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
   }
 }
 
-// V [bg][n][D] -> V^T [bg][D][n], 64-key tiles through LDS.
+// V [bg][n][D] -> V^T [bg][D][n], 64-key tiles through LDS; also the largest
+// squared key norm of each KV head (kn2max[bg], as bits: non-negative floats
+// order like their bit patterns, so the integer maximum is the float maximum).
 template <int D>
 __global__ __launch_bounds__(NTHR) void transpose_v_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
-                                                           int n) {
+                                                           const uint16_t* __restrict__ k,
+                                                           unsigned* __restrict__ kn2max, int n) {
   __shared__ uint16_t tile[KS][D + 2];
   const int64_t bg = blockIdx.y;
   const int key0 = blockIdx.x * KS;
@@ -1055,10 +1134,29 @@ __global__ __launch_bounds__(NTHR) void transpose_v_kernel(const uint16_t* __res
     u.w = tile[kc * 8 + 6][d] | ((uint32_t)tile[kc * 8 + 7][d] << 16);
     st16(dst + (size_t)d * n + kc * 8, u);
   }
+  // squared norms of the same 64 keys: the CPR threads of a key row are adjacent lanes
+  const uint16_t* ksrc = k + ((size_t)bg * n + key0) * D;
+  float best = 0.f;
+  for (int c = threadIdx.x; c < KS * CPR; c += NTHR) {
+    const uint4 u = ld16(ksrc + (size_t)(c / CPR) * D + (c % CPR) * 8);
+    const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x2 x = __builtin_bit_cast(bf16x2, wds[j]);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
+    }
+#pragma unroll
+    for (int msk = CPR / 2; msk >= 1; msk >>= 1) acc += xor_shfl(acc, msk);
+    best = fmaxf(best, acc);
+  }
+  best = wave_max(best);
+  if (lane_id() == 0) atomicMax(&kn2max[bg], __float_as_uint(best));
 }
 
-__global__ void zero_counters_kernel(int* __restrict__ c) {
+__global__ void zero_counters_kernel(int* __restrict__ c, unsigned* __restrict__ kn2max, int nkv) {
   if (threadIdx.x < NXCD) c[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < nkv; i += blockDim.x) kn2max[i] = 0u;
 }
 
 int cu_count() {
@@ -1076,29 +1174,33 @@ int cu_count() {
 constexpr size_t COUNTER_BYTES = 256;
 
 size_t vt_bytes(const Dims& dm) { return (size_t)dm.batch * dm.h_kv * dm.n * dm.d * 2; }
+// largest squared key norm per KV head, padded to 256 bytes
+size_t kn2_bytes(const Dims& dm) { return ((size_t)dm.batch * dm.h_kv * 4 + 255) & ~(size_t)255; }
 
 template <int D, bool DENSE>
 hipError_t attn_launch(const Dims& dm, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const int64_t* row_ptr, const int32_t* col_idx, int64_t cap, void* out,
                        int out_bf16, void* ws, hipStream_t st) {
   int* counters = static_cast<int*>(ws);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + COUNTER_BYTES);
+  unsigned* kn2 = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + COUNTER_BYTES);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + COUNTER_BYTES + kn2_bytes(dm));
+  const float* kn2f = reinterpret_cast<const float*>(kn2);
   const float c2 = LOG2E / sqrtf((float)D);
   const Queue qd = make_queue(dm.nb, dm.bh);
   const int64_t slots = (int64_t)(cu_count() * WG_PER_CU + NXCD - 1) / NXCD * NXCD;
   const int64_t items = qd.per_queue * NXCD;
   const unsigned grid = (unsigned)(items < slots ? items : slots);
-  zero_counters_kernel<<<1, 64, 0, st>>>(counters);
-  transpose_v_kernel<D><<<dim3(dm.n / KS, (unsigned)(dm.batch * dm.h_kv)), NTHR, 0, st>>>(v, vt, dm.n);
+  zero_counters_kernel<<<1, 256, 0, st>>>(counters, kn2, dm.batch * dm.h_kv);
+  transpose_v_kernel<D><<<dim3(dm.n / KS, (unsigned)(dm.batch * dm.h_kv)), NTHR, 0, st>>>(v, vt, k, kn2, dm.n);
   if constexpr (D == 128) {
     const int64_t slots64 = (int64_t)(cu_count() * Q64_WG_PER_CU + NXCD - 1) / NXCD * NXCD;
     const unsigned grid64 = (unsigned)(items < slots64 ? items : slots64);
     if (out_bf16)
       attn_q64_kernel<DENSE, true><<<grid64, Q64_THR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
-                                                               dm.group, qd, counters, c2);
+                                                               dm.group, qd, counters, kn2f, c2);
     else
       attn_q64_kernel<DENSE, false><<<grid64, Q64_THR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
-                                                                dm.group, qd, counters, c2);
+                                                                dm.group, qd, counters, kn2f, c2);
   } else {
     if (out_bf16)
       attn_kernel<D, DENSE, true><<<grid, NTHR, 0, st>>>(q, k, vt, row_ptr, col_idx, cap, out, dm.n, dm.h_q,
@@ -1112,7 +1214,7 @@ hipError_t attn_launch(const Dims& dm, const uint16_t* q, const uint16_t* k, con
 
 }  // namespace
 
-size_t attn_ws_bytes(const Dims& dm) { return COUNTER_BYTES + vt_bytes(dm); }
+size_t attn_ws_bytes(const Dims& dm) { return COUNTER_BYTES + kn2_bytes(dm) + vt_bytes(dm); }
 
 hipError_t launch_sparse_attn(const Dims& dm, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int64_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,

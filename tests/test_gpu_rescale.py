@@ -1,12 +1,16 @@
 """GPU parity on inputs whose row maxima keep growing along the keys.
 
-The attention kernels keep a reference maximum per query row and raise it
-(rescaling the row's output and row sum) only when a stage's maximum exceeds it
-by more than 2^8 in log2 units.  On the workload recipe the sink block comes
-first in every row and usually holds the maximum, so that branch seldom runs
-there.  Here the keys are scaled up block by block, with an extra jump four
-blocks before the end, so rows raise their reference several times, by small
-and by large steps, at both head dims, through dense_attn and sparse_attn.
+The attention kernels keep a reference maximum per query row.  At d = 128 a
+wave whose rows' Cauchy-Schwarz logit bound (c2 |q| max|k|) lies at most 64
+log2 units above the first stage's maximum keeps that maximum for the whole
+row; otherwise it tracks the maximum and raises it (rescaling the row's output
+and row sum) when a stage's maximum exceeds it by more than 2^8.  At d = 64
+every row tracks.  On the workload recipe every wave keeps its first maximum.
+Here the keys are scaled up block by block, with an extra jump four blocks
+before the end, so rows raise their reference several times, by small and by
+large steps, at both head dims, through dense_attn and sparse_attn; a third
+shape mixes one KV head of such keys with one of plain keys, so that one launch
+runs waves of both kinds.
 """
 import numpy as np
 import pytest
@@ -23,20 +27,50 @@ pytestmark = pytest.mark.gpu
 SHAPES = {
     "d128_gqa2": Shape(1, 2048, 2, 1, 128),
     "d64_mha": Shape(1, 2048, 2, 2, 64),
+    "d128_mixed": Shape(1, 2048, 4, 2, 128),
 }
 STAGE = 64
 RAISE_LOG2 = 8.0
+FIXED_SPAN = 64.0
 
 
 def _growing_inputs(sh, seed):
+    """Keys scaled up block by block; in the mixed shape only KV head 1's."""
     inp = make_inputs(sh, vs_fraction=0.5, sink_scale=3.0, n_vert=4, seed=seed)
     nb = sh.n_blocks
     kb = np.arange(sh.n) // 128
     g = 1.0 + 0.4 * kb
     g[kb == nb - 4] *= 3.0
-    k = bf16_bits_to_f32(inp["k"]) * g[None, None, :, None].astype(np.float32)
+    gk = np.ones((sh.h_kv, sh.n), dtype=np.float32)
+    gk[1 if sh is SHAPES["d128_mixed"] else 0:] = g
+    k = bf16_bits_to_f32(inp["k"]) * gk[None, :, :, None]
     inp["k"] = f32_to_bf16_bits(k)
     return inp
+
+
+def _tracking_waves(inp, sh, rows_by_head):
+    """(waves that track their maxima, waves that keep the first one) at d = 128,
+    from the rule the kernel applies (64 query rows per wave)."""
+    c2 = np.log2(np.e) / np.sqrt(sh.d)
+    G = sh.h_q // sh.h_kv
+    track = keep = 0
+    for (b, h), rows in rows_by_head.items():
+        q = bf16_bits_to_f32(inp["q"][b, h]).astype(np.float64)
+        k = bf16_bits_to_f32(inp["k"][b, h // G]).astype(np.float64)
+        kn = np.sqrt((k * k).sum(axis=1).max())
+        for qb, cols in enumerate(rows):
+            c = int(sorted(cols)[0])
+            for w in range(2):
+                rr = qb * 128 + 64 * w + np.arange(64)
+                s = (q[rr] @ k[c * 128:c * 128 + STAGE].T) * c2
+                if c == qb:
+                    s = np.where(c * 128 + np.arange(STAGE)[None, :] > rr[:, None], -np.inf, s)
+                bound = c2 * np.sqrt((q[rr] * q[rr]).sum(axis=1)) * kn
+                if np.any(bound - s.max(axis=1) > FIXED_SPAN):
+                    track += 1
+                else:
+                    keep += 1
+    return track, keep
 
 
 def _raises(inp, sh, rows_by_head):
@@ -73,6 +107,9 @@ def test_dense_with_growing_maxima(name):
     inp = _growing_inputs(sh, seed=81)
     rows = {(0, h): co.dense_rows(sh.n_blocks) for h in range(sh.h_q)}
     assert _raises(inp, sh, rows) > 4 * sh.h_q
+    if sh.d == 128:
+        track, keep = _tracking_waves(inp, sh, rows)
+        assert track > 0 and keep > 0, (track, keep)
     q, k, v = device_inputs(inp)
     out = crisp.dense_attn(q, k, v)
     torch.cuda.synchronize()
@@ -95,6 +132,9 @@ def test_sparse_with_growing_maxima(name):
         rows_all.extend(per)
         rows[(0, h)] = [np.array(r, dtype=np.int64) for r in per]
     assert _raises(inp, sh, rows) > 2 * sh.h_q
+    if sh.d == 128:
+        track, keep = _tracking_waves(inp, sh, rows)
+        assert track > 0 and keep > 0, (track, keep)
     row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows_all])]).astype(np.int64)
     col = np.array([c for r in rows_all for c in r], dtype=np.int32)
     sel = dict(row_ptr=torch.from_numpy(row_ptr).cuda(), col_idx=torch.from_numpy(col).cuda())
