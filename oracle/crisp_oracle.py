@@ -424,12 +424,3 @@ def flex_head(q_h, k_g, *, tau_jsd=0.1, gamma=0.95, k_min_tokens=1024, block=BLO
         res.update(pe=pe, rows=pe["rows"])
     return res
 
-
-def rows_to_csr(rows_per_head):
-    """Concatenate per-head row lists into (row_ptr int64, col_idx int32)."""
-    counts = [len(r) for rows in rows_per_head for r in rows]
-    row_ptr = np.zeros(len(counts) + 1, dtype=np.int64)
-    np.cumsum(counts, out=row_ptr[1:])
-    col = np.concatenate([r for rows in rows_per_head for r in rows]).astype(np.int32) \
-        if counts else np.zeros(0, np.int32)
-    return row_ptr, col

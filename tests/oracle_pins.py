@@ -497,3 +497,95 @@ def check_pe_per_row_brute_force(co, seed=31):
             order = sorted(range(r + 1), key=lambda j: (-row[j], j))
             want = set(order[:best]) | {r}
             assert set(pe["rows"][r].tolist()) == want, (trial, r)
+
+
+# --- the layer driver: GQA head map, head subsets, forced routes, row subsets ------
+# These take the driver module (``dcheck_*``): the layer driver produces every
+# expected value of the GPU parity tests, so its query-head -> KV-head map and its
+# query-row selection are pinned here against formulations that do not share it:
+# K and V repeated per query head (torch's repeat_interleave / numpy's repeat).
+def _gqa_bits(seed, batch=2, h_q=8, h_kv=2, n=384, d=32, q_scale=1.5):
+    from prefill_inputs import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    q = f32_to_bf16_bits((rng.standard_normal((batch, h_q, n, d)) * q_scale).astype(np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((batch, h_kv, n, d)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((batch, h_kv, n, d)).astype(np.float32))
+    return q, k, v
+
+
+def dcheck_layer_attention_gqa(drv, seed=40):
+    """layer_attention on a GQA layer (batch 2, 8 query heads on 2 KV heads) equals
+    torch's scaled_dot_product_attention (float64, CPU) with K and V repeated per
+    query head and the explicit causal-and-selected token mask, on chosen query
+    blocks and on chosen rows inside them."""
+    import torch
+    from prefill_inputs import bf16_bits_to_f32
+    q, k, v = _gqa_bits(seed)
+    nbat, H, n, d = q.shape
+    G = H // k.shape[1]
+    nb = n // B
+    rng = np.random.default_rng(seed + 1)
+    rows_of, blocks_of = {}, {}
+    for b in range(nbat):
+        for h in range(H):
+            rows_of[(b, h)] = [np.array(sorted(set(rng.choice(qb + 1, size=int(rng.integers(1, qb + 2)),
+                                                              replace=False).tolist()) | {qb}))
+                               for qb in range(nb)]
+            blocks_of[(b, h)] = [0, nb - 1] if (b + h) % 2 else [1]
+    q_rows = [0, 5, 64, 127]
+    got = drv.layer_attention(q, k, v, rows_of, blocks_of, workers=2, q_rows=q_rows)
+    qt = torch.from_numpy(bf16_bits_to_f32(q).astype(np.float64))
+    kt = torch.from_numpy(bf16_bits_to_f32(k).astype(np.float64)).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(bf16_bits_to_f32(v).astype(np.float64)).repeat_interleave(G, dim=1)
+    mask = np.zeros((nbat, H, n, n), dtype=bool)
+    for (b, h), rows in rows_of.items():
+        for qb, cols in enumerate(rows):
+            for kb in cols:
+                mask[b, h, qb * B:(qb + 1) * B, kb * B:(kb + 1) * B] = True
+    mask &= np.tril(np.ones((n, n), dtype=bool))
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask)).numpy()
+    assert set(got) == {(b, h, qb) for (b, h), qbs in blocks_of.items() for qb in qbs}
+    for (b, h, qb), o in got.items():
+        want = ref[b, h, qb * B + np.asarray(q_rows)]
+        assert o.shape == want.shape, (b, h, qb)
+        assert np.allclose(o, want, rtol=1e-10, atol=1e-12), (b, h, qb)
+
+
+def _selection_case(seed):
+    q, k, _ = _gqa_bits(seed, n=768, q_scale=3.0)
+    G = q.shape[1] // k.shape[1]
+    return q, k, np.repeat(k, G, axis=1)   # kq[b, h]: the keys query head h reads
+
+
+def dcheck_layer_selection_gqa(drv, seed=41):
+    """layer_selection on a GQA layer matches crisp_head run head by head on the
+    keys repeated per query head; a head subset and a forced route are honoured."""
+    from oracle import crisp_oracle as co
+    q, k, kq = _selection_case(seed)
+    heads = [(0, 1), (0, 6), (1, 3), (1, 4)]
+    got = drv.layer_selection(q, k, heads=heads, force_vs={(1, 3): False}, workers=2)
+    assert sorted(got) == sorted(heads)
+    for (b, h), r in got.items():
+        ref = co.crisp_head(co.bf16_to_f64(q[b, h]), co.bf16_to_f64(kq[b, h]),
+                            force_vs=False if (b, h) == (1, 3) else None)
+        assert r["c_struct"] == ref["c_struct"] and r["is_vs"] == ref["is_vs"], (b, h)
+        assert all(np.array_equal(x, y) for x, y in zip(r["rows"], ref["rows"])), (b, h)
+    # on this short layer every head routes VS by itself (local window); the forced one is PE
+    assert not got[(1, 3)]["is_vs"] and got[(0, 1)]["is_vs"]
+
+
+def dcheck_layer_selection_flex_gqa(drv, seed=42):
+    """layer_selection_flex on a GQA layer matches flex_head run head by head on
+    the keys repeated per query head; a head subset and a forced route are honoured."""
+    from oracle import crisp_oracle as co
+    q, k, kq = _selection_case(seed)
+    heads = [(0, 1), (0, 4), (1, 2), (1, 6)]
+    got = drv.layer_selection_flex(q, k, heads=heads, force_vs={(0, 4): True}, workers=2)
+    assert sorted(got) == sorted(heads)
+    for (b, h), r in got.items():
+        ref = co.flex_head(co.bf16_to_f64(q[b, h]), co.bf16_to_f64(kq[b, h]),
+                           force_vs=True if (b, h) == (0, 4) else None)
+        assert r["jsd"] == ref["jsd"] and r["is_vs"] == ref["is_vs"], (b, h)
+        assert all(np.array_equal(x, y) for x, y in zip(r["rows"], ref["rows"])), (b, h)
+    # Gaussian heads route PE under the JSD router; the forced one is VS
+    assert got[(0, 4)]["is_vs"] and not got[(0, 1)]["is_vs"]

@@ -240,15 +240,16 @@ def gpu_flex_layer(q, k, v, cfg, tau_jsd, attn=True):
 
 
 def check_flex_route(g, ora, H, tau_jsd):
-    """D_JS to JSD_RTOL of the oracle's; the pattern exact unless D_JS is within
-    1e-4 relative of tau_jsd.  Returns {(b,h): gpu pattern} for exempt heads."""
+    """D_JS to JSD_RTOL of the oracle's; the pattern exact unless the oracle's
+    D_JS is within 1e-5 relative of tau_jsd (the routing rule of CRISP's router).
+    Returns {(b,h): gpu pattern} for exempt heads."""
     exempt = {}
     for (b, h), r in ora.items():
         i = b * H + h
         j_o = r["jsd"]
         assert abs(g["jsd"][i] - j_o) <= JSD_RTOL * abs(j_o) + 1e-7, ((b, h), g["jsd"][i], j_o)
         gv = bool(g["pattern"][i])
-        if abs(j_o - tau_jsd) <= JSD_RTOL * tau_jsd:
+        if abs(j_o - tau_jsd) <= REL * tau_jsd:
             exempt[(b, h)] = gv
         else:
             assert gv == r["is_vs"], ((b, h), j_o)
@@ -257,8 +258,9 @@ def check_flex_route(g, ora, H, tau_jsd):
 
 def _gamma_exempt(p, j, gamma, kmin):
     """Block j may differ between the GPU's and the oracle's gamma-cumsum set when
-    the oracle's prefix mass next to it is within 1e-5 gamma of gamma, or its
-    score ties the score at the cut (or at the k_min boundary) within 1e-5."""
+    the oracle's prefix mass before it (which decides whether it is kept) is
+    within 1e-5 gamma of gamma, or its score ties the score at the cut (or at the
+    k_min boundary) within 1e-5 relative."""
     nb = len(p)
     order = np.lexsort((np.arange(nb), -p))
     cs = np.cumsum(p[order])
@@ -266,7 +268,7 @@ def _gamma_exempt(p, j, gamma, kmin):
     cnt = int(hit[0]) + 1 if len(hit) else nb
     pos = int(np.nonzero(order == j)[0][0])
     before = cs[pos - 1] if pos > 0 else 0.0
-    if abs(before - gamma) <= REL * gamma or abs(cs[pos] - gamma) <= REL * gamma:
+    if abs(before - gamma) <= REL * gamma:
         return True
     k = min(max(cnt, kmin), nb)
     edge = p[order[k - 1]]

@@ -8,7 +8,7 @@ import types
 import pytest
 
 import oracle_pins as pins
-from oracle import crisp_oracle
+from oracle import crisp_oracle, driver
 
 SRC = open(crisp_oracle.__file__).read()
 
@@ -55,6 +55,25 @@ MUTANTS = {
 
 CHECKS = [getattr(pins, n) for n in dir(pins) if n.startswith("check_")]
 
+# Mistakes planted in copies of the layer driver, each to be caught by a driver pin.
+DRIVER_SRC = open(driver.__file__).read()
+DRIVER_MUTANTS = {
+    "attn_k_head_mod": ("co.bf16_to_f64(k_bits[b, h // G]),\n                         co.bf16_to_f64(v_bits",
+                        "co.bf16_to_f64(k_bits[b, h % k_bits.shape[1]]),\n                         co.bf16_to_f64(v_bits"),
+    "attn_v_head_mod": ("co.bf16_to_f64(v_bits[b, h // G]))", "co.bf16_to_f64(v_bits[b, h % k_bits.shape[1]]))"),
+    "attn_q_rows_ignored": ("q_blocks=[qb], q_rows=q_rows)[qb]", "q_blocks=[qb])[qb]"),
+    "attn_q_rows_reversed": ("q_blocks=[qb], q_rows=q_rows)[qb]",
+                             "q_blocks=[qb], q_rows=None if q_rows is None else list(q_rows)[::-1])[qb]"),
+    "sel_head_mod": ("        k = co.bf16_to_f64(k_bits[b, h // G])\n        return bh, co.crisp_head(",
+                     "        k = co.bf16_to_f64(k_bits[b, h % k_bits.shape[1]])\n        return bh, co.crisp_head("),
+    "sel_force_ignored": ("force_vs=force_vs.get(bh), floor=floor", "force_vs=None, floor=floor"),
+    "flex_head_mod": ("        k = co.bf16_to_f64(k_bits[b, h // G])\n        return bh, co.flex_head(",
+                      "        k = co.bf16_to_f64(k_bits[b, h % k_bits.shape[1]])\n        return bh, co.flex_head("),
+    "flex_force_ignored": ("                                force_vs=force_vs.get(bh))",
+                           "                                force_vs=None)"),
+}
+DRIVER_CHECKS = [getattr(pins, n) for n in dir(pins) if n.startswith("dcheck_")]
+
 
 def _load(name, old, new):
     assert SRC.count(old) == 1, f"mutation {name} does not match the oracle source exactly once"
@@ -85,3 +104,28 @@ def test_mutant_is_caught(name):
 
 def test_real_oracle_passes_bf16_pin():
     _bf16_pin(crisp_oracle)
+
+
+def _load_driver(name, old, new):
+    assert DRIVER_SRC.count(old) == 1, f"mutation {name} does not match the driver source exactly once"
+    src = DRIVER_SRC.replace(old, new).replace("from . import crisp_oracle as co", "from oracle import crisp_oracle as co")
+    mod = types.ModuleType(f"driver_mutant_{name}")
+    exec(compile(src, f"<driver mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(DRIVER_MUTANTS))
+def test_driver_mutant_is_caught(name):
+    mod = _load_driver(name, *DRIVER_MUTANTS[name])
+    failed = []
+    for chk in DRIVER_CHECKS:
+        try:
+            chk(mod)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(chk.__name__)
+    assert failed, f"no driver pin catches mutant {name}"
+
+
+def test_real_driver_passes_driver_pins():
+    for chk in DRIVER_CHECKS:
+        chk(driver)
