@@ -77,7 +77,8 @@ enum crisp_status {
   CRISP_ERR_WORKSPACE = -5,   /* ws_bytes smaller than the size query gives */
   CRISP_ERR_CAPACITY = -6,    /* col_capacity below crisp_max_blocks        */
   CRISP_ERR_HIP = -7,         /* a HIP launch failed                        */
-  CRISP_ERR_ALIGN = -8        /* a device pointer is not 16-byte aligned    */
+  CRISP_ERR_ALIGN = -8,       /* a device pointer is not 16-byte aligned    */
+  CRISP_ERR_SCRATCH = -9      /* shape needs more than the static scratch   */
 };
 
 enum crisp_out_dtype { CRISP_OUT_F32 = 0, CRISP_OUT_BF16 = 1 };
@@ -114,6 +115,26 @@ int crisp_route(const crisp_shape* shape, const crisp_cfg* cfg,
                 const void* q_bf16, const void* k_bf16,
                 float* c_struct, int8_t* pattern, float* p_vert, float* p_slash,
                 void* ws, size_t ws_bytes, void* stream);
+
+/* crisp_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels, arguments and outputs as crisp_route, with the workspace
+ * replaced by a static device buffer of CRISP_ROUTE_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine); the
+ * caller still passes the inputs and outputs.  Shapes whose routing workspace
+ * (crisp_workspace_bytes(CRISP_CALL_ROUTE)) exceeds the buffer return
+ * CRISP_ERR_SCRATCH before any HIP call (16 MiB covers, e.g., 32 heads at
+ * 524288 tokens, about 5 MiB).  Every call on a GPU shares that GPU's buffer:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.  Nothing in the buffer needs clearing between
+ * calls: each kernel writes all of the scratch it later reads.  Other errors
+ * as crisp_route. */
+#define CRISP_ROUTE_SCRATCH_BYTES (16u << 20)
+int crisp_route_noalloc(const crisp_shape* shape, const crisp_cfg* cfg,
+                        const void* q_bf16, const void* k_bf16,
+                        float* c_struct, int8_t* pattern, float* p_vert, float* p_slash,
+                        void* stream);
 
 /* Index selection: VSIndex for pattern 1 heads, PEIndex for pattern 0 heads
  * (digest: method-steps section steps 2-3, Algorithm 3 and 4 captions, and the

@@ -19,7 +19,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["CrispError", "config", "shape_of", "workspace_bytes", "max_blocks", "use_dense", "route", "select",
+__all__ = ["CrispError", "config", "shape_of", "workspace_bytes", "max_blocks", "use_dense", "route",
+           "route_noalloc", "select",
            "sparse_attn", "dense_attn", "prefill", "flex_route", "flex_select", "flex_prefill", "library_path",
            "load"]
 
@@ -68,6 +69,7 @@ def load():
     lib.crisp_max_blocks.argtypes = [ps, ctypes.POINTER(I64)]
     lib.crisp_use_dense.argtypes = [ps, ctypes.POINTER(ctypes.c_int32)]
     lib.crisp_route.argtypes = [ps, pc, P, P, P, P, P, P, P, SZ, P]
+    lib.crisp_route_noalloc.argtypes = [ps, pc, P, P, P, P, P, P, P]
     lib.crisp_select.argtypes = [ps, pc, P, P, P, P, P, P, P, I64, P, P, SZ, P]
     lib.crisp_sparse_attn.argtypes = [ps, pc, P, P, P, P, P, I64, P, I, P, SZ, P]
     lib.dense_attn.argtypes = [ps, P, P, P, P, I, P, SZ, P]
@@ -78,7 +80,8 @@ def load():
     lib.crisp_status_string.argtypes = [I]
     lib.crisp_status_string.restype = ctypes.c_char_p
     lib.crisp_last_error.restype = ctypes.c_char_p
-    for f in ("crisp_workspace_bytes", "crisp_max_blocks", "crisp_use_dense", "crisp_route", "crisp_select",
+    for f in ("crisp_workspace_bytes", "crisp_max_blocks", "crisp_use_dense", "crisp_route", "crisp_route_noalloc",
+              "crisp_select",
               "crisp_sparse_attn", "dense_attn", "flex_route", "flex_select", "crisp_select_variant",
               "crisp_mfma_probe"):
         getattr(lib, f).restype = I
@@ -172,6 +175,25 @@ def route(q, k, cfg: Cfg | None = None, out: dict | None = None, ws=None, stream
     _check(load().crisp_route(ctypes.byref(sh), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(out["c_struct"]),
                               _ptr(out["pattern"]), _ptr(out["p_vert"]), _ptr(out["p_slash"]), _ptr(ws),
                               nws, _stream(stream)))
+    return out
+
+
+def route_noalloc(q, k, cfg: Cfg | None = None, out: dict | None = None, stream=None) -> dict:
+    """route() on the library's static device scratch (crisp_route_noalloc): no
+    workspace is allocated; pass ``out`` to allocate nothing at all."""
+    import torch
+    cfg = cfg or config()
+    _check_qkv(q, k)
+    sh = shape_of(q, k)
+    bh, nb = sh.batch * sh.h_q, sh.n // 128
+    dev = q.device
+    out = out or dict(c_struct=torch.empty(bh, dtype=torch.float32, device=dev),
+                      pattern=torch.empty(bh, dtype=torch.int8, device=dev),
+                      p_vert=torch.empty(bh, nb, dtype=torch.float32, device=dev),
+                      p_slash=torch.empty(bh, nb, dtype=torch.float32, device=dev))
+    _check(load().crisp_route_noalloc(ctypes.byref(sh), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(out["c_struct"]),
+                                      _ptr(out["pattern"]), _ptr(out["p_vert"]), _ptr(out["p_slash"]),
+                                      _stream(stream)))
     return out
 
 

@@ -149,6 +149,27 @@ int crisp_route(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf
                                         w.part, w.stats, w.lu, static_cast<hipStream_t>(stream)));
 }
 
+int crisp_route_noalloc(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
+                        float* c_struct, int8_t* pattern, float* p_vert, float* p_slash, void* stream) {
+  Dims dm;
+  int st = make_dims(shape, &dm);
+  if (st) return st;
+  if ((st = check_cfg(cfg))) return st;
+  if (dm.batch == 0) return CRISP_OK;
+  if (!q_bf16 || !k_bf16 || !c_struct || !pattern || !p_vert || !p_slash) return CRISP_ERR_NULL;
+  if (misaligned(q_bf16) || misaligned(k_bf16) || misaligned(c_struct) || misaligned(pattern) ||
+      misaligned(p_vert) || misaligned(p_slash))
+    return CRISP_ERR_ALIGN;
+  if (route_ws_layout(dm, nullptr, nullptr) > (size_t)CRISP_ROUTE_SCRATCH_BYTES) return CRISP_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((st = hip_status(crisp::route_scratch(&ws)))) return st;
+  RouteWs w;
+  route_ws_layout(dm, &w, static_cast<char*>(ws));
+  return hip_status(crisp::launch_route(dm, cfg->tau, static_cast<const uint16_t*>(q_bf16),
+                                        static_cast<const uint16_t*>(k_bf16), c_struct, pattern, p_vert, p_slash,
+                                        w.part, w.stats, w.lu, static_cast<hipStream_t>(stream)));
+}
+
 static int select_common(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
                          const int8_t* pattern, const float* p_vert, const float* p_slash, int64_t* row_ptr,
                          int32_t* col_idx, int64_t col_capacity, uint8_t* sel_mask, void* ws, size_t ws_bytes,
@@ -278,6 +299,7 @@ const char* crisp_status_string(int status) {
     case CRISP_ERR_CAPACITY: return "col_capacity below crisp_max_blocks";
     case CRISP_ERR_HIP: return "HIP launch failed";
     case CRISP_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case CRISP_ERR_SCRATCH: return "shape needs more scratch than the static routing buffer holds";
     default: return "unknown status";
   }
 }

@@ -23,6 +23,8 @@ int proxy_num_chunks(const Dims& dm);
 hipError_t launch_route(const Dims& dm, float tau, const uint16_t* q, const uint16_t* k,
                         float* c_struct, int8_t* pattern, float* p_vert, float* p_slash,
                         float* ws_part, float* ws_stats, float* ws_lu, hipStream_t st);
+// Device address of the current GPU's static routing scratch (CRISP_ROUTE_SCRATCH_BYTES).
+hipError_t route_scratch(void** ptr);
 
 // ---- selection (select.hip) ----
 struct SelectWs {

@@ -17,10 +17,45 @@
 // p_slash[kb] = (L_kb + U_{kb-1})/b.  Every reduction has a fixed order.
 #include <math.h>
 
+#include <mutex>
+
+#include "../../include/crisp.h"
 #include "crisp_internal.h"
 #include "tile_core.hpp"
 
 namespace crisp {
+
+// Device scratch of crisp_route_noalloc, for callers that cannot allocate: the
+// proxy passes' partial (max, sum) per chunk, the combined row statistics and
+// the L/U tile sums live here instead of in a caller's workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  Every kernel of
+// the routing pass writes all of the scratch it later reads, so nothing needs
+// clearing between calls; calls that overlap on one GPU race on it.
+static __device__ __align__(256) unsigned char scratch[CRISP_ROUTE_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+// Device address of this GPU's scratch (the current device's), looked up once
+// per device: in host code the array's name is only a stand-in for the symbol.
+hipError_t route_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

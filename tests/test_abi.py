@@ -11,7 +11,7 @@ import long_context_sparse_patsearch_amd as crisp
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "crisp.h")
 
-OK, NULL, SHAPE, PARAM, UNSUP, WS, CAP, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, PARAM, UNSUP, WS, CAP, HIP, ALIGN, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 FAKE = 0x10000          # an aligned address that is never dereferenced: validation fails first
 
 
@@ -216,3 +216,27 @@ def test_mfma_probe_rejects_before_any_hip_call(lib):
     assert lib.crisp_mfma_probe(FAKE + 8, FAKE, 10, ctypes.byref(flop), None) == ALIGN
     assert lib.crisp_mfma_probe(FAKE, FAKE, 0, ctypes.byref(flop), None) == PARAM
     assert lib.crisp_mfma_probe(FAKE, FAKE, 10 ** 7 + 1, ctypes.byref(flop), None) == PARAM
+
+
+def test_route_noalloc_validates_before_any_hip_call(lib):
+    """crisp_route_noalloc: bad arguments and shapes whose routing workspace exceeds the
+    static scratch are rejected on the host (these calls never reach the GPU)."""
+    P = ctypes.c_void_p
+    cfg = crisp.config()
+    args = [P(FAKE)] * 6 + [P(0)]
+    sh = shape(n=4096, h_q=2, h_kv=2, d=128)
+    assert lib.crisp_route_noalloc(ctypes.byref(sh), ctypes.byref(cfg), P(0), *args[1:]) == NULL
+    assert lib.crisp_route_noalloc(ctypes.byref(sh), ctypes.byref(cfg), P(FAKE + 4), *args[1:]) == ALIGN
+    assert lib.crisp_route_noalloc(ctypes.byref(shape(n=4096 + 64)), ctypes.byref(cfg), *args) == SHAPE
+    assert lib.crisp_route_noalloc(ctypes.byref(shape(batch=0)), ctypes.byref(cfg), *args) == OK
+    big = shape(batch=1, n=131072, h_q=1024, h_kv=8, d=128)
+    need = ctypes.c_size_t(0)
+    assert lib.crisp_workspace_bytes(ctypes.byref(big), ctypes.byref(cfg), 0, ctypes.byref(need)) == OK
+    assert need.value > 16 << 20
+    assert lib.crisp_route_noalloc(ctypes.byref(big), ctypes.byref(cfg), *args) == SCRATCH
+    # the layers the benchmark times fit
+    for fits in (shape(n=524288, h_q=32, h_kv=8, d=128), shape(n=262144, h_q=28, h_kv=4, d=128),
+                 shape(n=1 << 20, h_q=4, h_kv=1, d=128)):
+        assert lib.crisp_workspace_bytes(ctypes.byref(fits), ctypes.byref(cfg), 0, ctypes.byref(need)) == OK
+        assert need.value <= 16 << 20, need.value
+    assert lib.crisp_status_string(SCRATCH).decode().startswith("shape needs more scratch")
