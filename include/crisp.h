@@ -123,14 +123,15 @@ int crisp_route(const crisp_shape* shape, const crisp_cfg* cfg,
  * library holds on each GPU it runs on until the process ends.  The call
  * allocates nothing (no hipMalloc, hipFree or allocating library routine); the
  * caller still passes the inputs and outputs.  Shapes whose routing workspace
- * (crisp_workspace_bytes(CRISP_CALL_ROUTE)) exceeds the buffer return
- * CRISP_ERR_SCRATCH before any HIP call (16 MiB covers, e.g., 32 heads at
- * 524288 tokens, about 5 MiB).  Every call on a GPU shares that GPU's buffer:
+ * (crisp_workspace_bytes(CRISP_CALL_ROUTE), about 1.6 KiB per query head and
+ * key block) exceeds the buffer return CRISP_ERR_SCRATCH before any HIP call
+ * (64 MiB covers, e.g., 32 query heads at up to 131072 tokens; 32 heads at
+ * 524288 tokens need about 206 MiB).  Every call on a GPU shares that GPU's buffer:
  * calls that overlap on one GPU (other streams, other threads) race and must
  * be serialised by the caller.  Nothing in the buffer needs clearing between
  * calls: each kernel writes all of the scratch it later reads.  Other errors
  * as crisp_route. */
-#define CRISP_ROUTE_SCRATCH_BYTES (16u << 20)
+#define CRISP_ROUTE_SCRATCH_BYTES (64u << 20)
 int crisp_route_noalloc(const crisp_shape* shape, const crisp_cfg* cfg,
                         const void* q_bf16, const void* k_bf16,
                         float* c_struct, int8_t* pattern, float* p_vert, float* p_slash,

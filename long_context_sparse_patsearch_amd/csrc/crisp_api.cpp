@@ -56,11 +56,7 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct RouteWs {
-  float* part;
-  float* stats;
-  float* lu;
-};
+using RouteWs = crisp::RouteBufs;
 
 size_t route_ws_layout(const Dims& dm, RouteWs* w, char* base) {
   const int nch = crisp::proxy_num_chunks(dm);
@@ -73,6 +69,7 @@ size_t route_ws_layout(const Dims& dm, RouteWs* w, char* base) {
   RouteWs r{};
   r.part = (float*)take((size_t)dm.bh * nch * kBlock * 2 * sizeof(float));
   r.stats = (float*)take((size_t)dm.bh * kBlock * 2 * sizeof(float));
+  r.tile = (float*)take((size_t)dm.bh * dm.nb * 3 * kBlock * sizeof(float));
   r.lu = (float*)take((size_t)dm.bh * dm.nb * 2 * sizeof(float));
   if (w) *w = r;
   return off;
@@ -146,7 +143,7 @@ int crisp_route(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf
   if (ws_bytes < route_ws_layout(dm, &w, static_cast<char*>(ws))) return CRISP_ERR_WORKSPACE;
   return hip_status(crisp::launch_route(dm, cfg->tau, static_cast<const uint16_t*>(q_bf16),
                                         static_cast<const uint16_t*>(k_bf16), c_struct, pattern, p_vert, p_slash,
-                                        w.part, w.stats, w.lu, static_cast<hipStream_t>(stream)));
+                                        w, static_cast<hipStream_t>(stream)));
 }
 
 int crisp_route_noalloc(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,
@@ -167,7 +164,7 @@ int crisp_route_noalloc(const crisp_shape* shape, const crisp_cfg* cfg, const vo
   route_ws_layout(dm, &w, static_cast<char*>(ws));
   return hip_status(crisp::launch_route(dm, cfg->tau, static_cast<const uint16_t*>(q_bf16),
                                         static_cast<const uint16_t*>(k_bf16), c_struct, pattern, p_vert, p_slash,
-                                        w.part, w.stats, w.lu, static_cast<hipStream_t>(stream)));
+                                        w, static_cast<hipStream_t>(stream)));
 }
 
 static int select_common(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf16, const void* k_bf16,

@@ -20,9 +20,15 @@ struct Dims {
 // Split of the key range into chunks for the proxy passes.
 int proxy_chunk_tiles(const Dims& dm);
 int proxy_num_chunks(const Dims& dm);
+struct RouteBufs {
+  float* part;    // [bh][chunks][128][2]  per row and chunk: maximum, normaliser
+  float* stats;   // [bh][128][2]          per row: maximum, 1 / normaliser
+  float* tile;    // [bh][nb][3][128]      per tile and row: maximum, lower and upper sums
+  float* lu;      // [bh][nb][2]           per key block: L, U
+};
 hipError_t launch_route(const Dims& dm, float tau, const uint16_t* q, const uint16_t* k,
                         float* c_struct, int8_t* pattern, float* p_vert, float* p_slash,
-                        float* ws_part, float* ws_stats, float* ws_lu, hipStream_t st);
+                        const RouteBufs& ws, hipStream_t st);
 // Device address of the current GPU's static routing scratch (CRISP_ROUTE_SCRATCH_BYTES).
 hipError_t route_scratch(void** ptr);
 

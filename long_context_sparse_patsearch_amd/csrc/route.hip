@@ -7,14 +7,19 @@
 // C_struct >= tau), and method-steps step 2 / Algorithm 3 caption (column and
 // diagonal means of A_hat, block-pooled).
 //
-// A_hat (b x n per head) is never stored.  Pass 1 computes per proxy row the
-// softmax max and normaliser over key chunks; a combine step merges chunks in
-// a fixed order; pass 2 recomputes each 128x128 proxy tile, normalises it and
-// sums its lower triangle with diagonal (in-tile key jj <= row i) into L and its
-// strict upper triangle into U.  Because b equals the block size, an entry of
-// key block kb lies on a diagonal t = j + b-1-i in slash block kb when jj <= i
-// and kb+1 otherwise, so p_vert[kb] = (L_kb + U_kb)/b and
-// p_slash[kb] = (L_kb + U_{kb-1})/b.  Every reduction has a fixed order.
+// A_hat (b x n per head) is never stored.  One pass over K computes every
+// 128x128 proxy tile once (up to four query heads of a KV group per workgroup,
+// so each K tile is read once for all of them) and keeps, per proxy row and
+// tile, the tile's maximum logit and the sums of the row's exponentials over
+// the tile's lower triangle with diagonal (in-tile key jj <= row i) and over
+// its strict upper triangle, plus per row and chunk of tiles the chunk's
+// maximum and normaliser.  A combine step merges the chunks into each row's
+// softmax statistics in a fixed order, and a reduction then normalises the
+// tile sums and adds them over the rows into L and U per key block.  Because b
+// equals the block size, an entry of key block kb lies on a diagonal
+// t = j + b-1-i in slash block kb when jj <= i and kb+1 otherwise, so
+// p_vert[kb] = (L_kb + U_kb)/b and p_slash[kb] = (L_kb + U_{kb-1})/b.  Every
+// reduction has a fixed order.
 #include <math.h>
 
 #include <mutex>
@@ -61,61 +66,163 @@ namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <int D>
-__global__ __launch_bounds__(NTHR) void proxy_stats_kernel(
+// The proxy pass over a chunk of key tiles, for HPW query heads of one KV
+// group at once: the workgroup is HPW slots of four waves, slot s holding the
+// 128 proxy rows of query head split*HPW + s of the group (wave w of a slot:
+// rows 32w..32w+31), so each K tile staged in LDS serves every head of the slot
+// set and K is read once per HPW heads.  Tiles are staged through registers
+// two tiles ahead into two LDS buffers (one barrier per tile).  Slots past the
+// group's last head only help stage the tiles.
+//
+// Per proxy row i and key tile kb it writes the tile's maximum logit m (log2
+// units) and the sums of 2^(logit - m) over the tile's lower triangle with
+// diagonal (in-tile key jj <= i) and over its strict upper triangle, to
+// tilep[bh][kb][3][128]; per row and chunk, the chunk's maximum and normaliser
+// to part[bh][chunk][row].  One pass over K thus holds everything the block
+// scores need once the rows' softmax statistics are known.
+template <int D, int HPW>
+__global__ __launch_bounds__(NTHR * HPW) void proxy_tile_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, float* __restrict__ part,
-    int n, int h_q, int group, int chunk_tiles, int nchunks, float c2) {
-  __shared__ __align__(16) uint16_t klds[Tile<D>::KLDS];
+    float* __restrict__ tilep, int n, int h_q, int group, int chunk_tiles, int nchunks, float c2) {
+  constexpr int NT = NTHR * HPW;
+  constexpr int CPR = Tile<D>::CPR;
+  constexpr int KCH = BLK * CPR / NT;   // 16-byte K loads per thread per tile
+  static_assert(KCH >= 1 && BLK * CPR % NT == 0, "tile staging");
+  __shared__ __align__(16) uint16_t klds[2][Tile<D>::KLDS];
   const int chunk = blockIdx.x;
-  const int64_t bh = blockIdx.y;
-  const int b = (int)(bh / h_q), h = (int)(bh % h_q);
-  const int h_kv = h_q / group, g = h / group;
-  const int nb = n / BLK, qb = nb - 1;
-  const uint16_t* qh = q + (size_t)bh * n * D;
-  const uint16_t* kg = k + ((size_t)b * h_kv + g) * n * D;
+  const int bg = blockIdx.y;             // batch * h_kv + KV head
+  const int h_kv = h_q / group;
+  const int b = bg / h_kv, g = bg % h_kv;
   const int w = wave_id(), lane = lane_id();
-  const int qloc = 32 * w + (lane & 31);
+  const int slot = w >> 2, wh = w & 3;
+  const int hg = blockIdx.z * HPW + slot;
+  const bool active = hg < group;
+  const int64_t bh = (int64_t)b * h_q + (int64_t)g * group + (active ? hg : 0);
+  const int nb = n / BLK, qb = nb - 1;
+  const int qloc = 32 * wh + (lane & 31);
+  const uint16_t* kg = k + (size_t)bg * n * D;
 
   bf16x8 qf[Tile<D>::NSTEP];
-  load_q_operands<D>(qh + (size_t)(qb * BLK + 32 * w) * D, qf);
+  if (active) load_q_operands<D>(q + ((size_t)bh * n + (size_t)qb * BLK + 32 * wh) * D, qf);
+  float mc = -INFINITY, lc = 0.f;      // the chunk's running maximum and normaliser of the row
 
-  float m = -INFINITY, l = 0.f;
-  const int kb0 = chunk * chunk_tiles, kb1 = min(nb, kb0 + chunk_tiles);
-  uint4 kr[Tile<D>::KCH];
-  load_k_regs<D>(kg + (size_t)kb0 * BLK * D, kr);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    store_k_lds<D>(klds, kr);
-    __syncthreads();
-    if (kb + 1 < kb1) load_k_regs<D>(kg + (size_t)(kb + 1) * BLK * D, kr);
-    f32x16 s[4];
-    qk_tile<D>(klds, qf, s);
+  auto load = [&](int kb, uint4 (&r)[KCH]) {
+    const uint16_t* t = kg + (size_t)kb * BLK * D;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = i * NT + threadIdx.x;
+      r[i] = ld16(t + (size_t)(c / CPR) * D + (c % CPR) * 8);
+    }
+  };
+  auto store = [&](uint16_t* lds, const uint4 (&r)[KCH]) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = i * NT + threadIdx.x;
+      st16(lds + (c / CPR) * Tile<D>::KSTR + (c % CPR) * 8, r[i]);
+    }
+  };
+  auto compute = [&](int kb, const uint16_t* lds) {
+    const uint16_t* base = lds + key_row_of_lane(lane & 31) * Tile<D>::KSTR + 8 * (lane >> 5);
     const bool diag = (kb == qb);
-    float tmax = -INFINITY;
+    float hm[2], hlo[2], hup[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int hf = 0; hf < 2; ++hf) {   // keys 64 hf .. 64 hf + 63, relative to their own maximum
+      f32x16 s[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[ks][r] * c2;
-        if (diag && 32 * ks + key_of_reg(r, lane) > qloc) x = -INFINITY;
-        s[ks][r] = x;
-        tmax = fmaxf(tmax, x);
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ks = 2 * hf + kk;
+        f32x16 acc = {};
+        const uint16_t* pp = base + 32 * ks * Tile<D>::KSTR;
+#pragma unroll
+        for (int st = 0; st < Tile<D>::NSTEP; ++st) acc = mfma_32x32x16(as_bf16x8(ld16(pp + 16 * st)), qf[st], acc);
+        s[kk] = acc;
       }
-    tmax = fmaxf(tmax, xor_shfl(tmax, 32));
-    const float mn = fmaxf(m, tmax);
-    float acc = 0.f;
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc += fast_exp2(s[ks][r] - mn);
-    l = l * fast_exp2(m - mn) + acc;
-    m = mn;
+        for (int r = 0; r < 16; ++r) {
+          float x = s[kk][r] * c2;
+          if (diag && 32 * (2 * hf + kk) + key_of_reg(r, lane) > qloc) x = -INFINITY;
+          s[kk][r] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, xor_shfl(tmax, 32));
+      // a half the causal mask hides entirely (diagonal tile, rows < 64) sums to 0
+      const float ref = tmax == -INFINITY ? 0.f : tmax;
+      float lo = 0.f, up = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(s[kk][r] - ref);
+          if (32 * (2 * hf + kk) + key_of_reg(r, lane) <= qloc) lo += e; else up += e;
+        }
+      hm[hf] = tmax;
+      hlo[hf] = lo + xor_shfl(lo, 32);
+      hup[hf] = up + xor_shfl(up, 32);
+    }
+    const float mt = fmaxf(hm[0], hm[1]);   // finite: key 0 of every tile is visible to every row
+    const float f0 = fast_exp2(hm[0] - mt), f1 = fast_exp2(hm[1] - mt);
+    const float lo = hlo[0] * f0 + hlo[1] * f1, up = hup[0] * f0 + hup[1] * f1;
+    const float mn = fmaxf(mc, mt);
+    lc = lc * fast_exp2(mc - mn) + (lo + up) * fast_exp2(mt - mn);
+    mc = mn;
+    if (lane < 32) {
+      float* o = tilep + ((size_t)bh * nb + kb) * 3 * BLK + qloc;
+      o[0] = mt;
+      o[BLK] = lo;
+      o[2 * BLK] = up;
+    }
+  };
+
+  const int kb0 = chunk * chunk_tiles, kb1 = min(nb, kb0 + chunk_tiles);
+  uint4 r0[KCH], r1[KCH];
+  load(kb0, r0);
+  if (kb0 + 1 < kb1) load(kb0 + 1, r1);
+  for (int kb = kb0; kb < kb1; kb += 2) {
+    // tile kb: registers r0, buffer 0
+    store(klds[0], r0);
     __syncthreads();
+    if (kb + 2 < kb1) load(kb + 2, r0);
+    if (active) compute(kb, klds[0]);
+    if (kb + 1 >= kb1) break;
+    // tile kb + 1: registers r1, buffer 1
+    store(klds[1], r1);
+    __syncthreads();
+    if (kb + 3 < kb1) load(kb + 3, r1);
+    if (active) compute(kb + 1, klds[1]);
   }
-  l += xor_shfl(l, 32);
-  if (lane < 32) {
+  if (active && lane < 32) {
     float* o = part + (((size_t)bh * nchunks + chunk) * BLK + qloc) * 2;
-    o[0] = m;
-    o[1] = l;
+    o[0] = mc;
+    o[1] = lc;
+  }
+}
+
+// Block sums of the normalised proxy: per (head, key tile kb), over the 128
+// proxy rows i, L = sum_i lo_i 2^(m_i - M_i) / L_i and U likewise from up_i,
+// with (M_i, 1/L_i) the rows' combined statistics.  One wave per tile, rows i
+// and i + 64 in lane i, then a fixed-order butterfly.
+__global__ __launch_bounds__(NTHR) void proxy_reduce_kernel(const float* __restrict__ tilep,
+                                                            const float* __restrict__ stats, float* __restrict__ lu,
+                                                            int nb) {
+  const int64_t bh = blockIdx.y;
+  const int lane = lane_id();
+  const float* st = stats + (size_t)bh * BLK * 2;
+  const float M0 = st[2 * lane], iL0 = st[2 * lane + 1];
+  const float M1 = st[2 * (lane + 64)], iL1 = st[2 * (lane + 64) + 1];
+  for (int kb = blockIdx.x * 4 + wave_id(); kb < nb; kb += gridDim.x * 4) {
+    const float* t = tilep + ((size_t)bh * nb + kb) * 3 * BLK;
+    const float w0 = fast_exp2(t[lane] - M0) * iL0, w1 = fast_exp2(t[lane + 64] - M1) * iL1;
+    float lo = t[BLK + lane] * w0 + t[BLK + lane + 64] * w1;
+    float up = t[2 * BLK + lane] * w0 + t[2 * BLK + lane + 64] * w1;
+    lo = wave_sum(lo);
+    up = wave_sum(up);
+    if (lane == 0) {
+      lu[((size_t)bh * nb + kb) * 2] = lo;
+      lu[((size_t)bh * nb + kb) * 2 + 1] = up;
+    }
   }
 }
 
@@ -134,62 +241,6 @@ __global__ __launch_bounds__(BLK) void proxy_combine_kernel(const float* __restr
   for (int c = 0; c < nchunks; ++c) L += p[(size_t)c * BLK * 2 + 1] * fast_exp2(p[(size_t)c * BLK * 2] - M);
   stats[((size_t)bh * BLK + i) * 2] = M;
   stats[((size_t)bh * BLK + i) * 2 + 1] = 1.f / L;
-}
-
-template <int D>
-__global__ __launch_bounds__(NTHR) void proxy_pool_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ stats,
-    float* __restrict__ lu, int n, int h_q, int group, int chunk_tiles, float c2) {
-  __shared__ __align__(16) uint16_t klds[Tile<D>::KLDS];
-  __shared__ float red[4][2];
-  const int chunk = blockIdx.x;
-  const int64_t bh = blockIdx.y;
-  const int b = (int)(bh / h_q), h = (int)(bh % h_q);
-  const int h_kv = h_q / group, g = h / group;
-  const int nb = n / BLK, qb = nb - 1;
-  const uint16_t* qh = q + (size_t)bh * n * D;
-  const uint16_t* kg = k + ((size_t)b * h_kv + g) * n * D;
-  const int w = wave_id(), lane = lane_id();
-  const int qloc = 32 * w + (lane & 31);
-  const float M = stats[((size_t)bh * BLK + qloc) * 2];
-  const float invL = stats[((size_t)bh * BLK + qloc) * 2 + 1];
-
-  bf16x8 qf[Tile<D>::NSTEP];
-  load_q_operands<D>(qh + (size_t)(qb * BLK + 32 * w) * D, qf);
-
-  const int kb0 = chunk * chunk_tiles, kb1 = min(nb, kb0 + chunk_tiles);
-  uint4 kr[Tile<D>::KCH];
-  load_k_regs<D>(kg + (size_t)kb0 * BLK * D, kr);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    store_k_lds<D>(klds, kr);
-    __syncthreads();
-    if (kb + 1 < kb1) load_k_regs<D>(kg + (size_t)(kb + 1) * BLK * D, kr);
-    f32x16 s[4];
-    qk_tile<D>(klds, qf, s);
-    const bool diag = (kb == qb);
-    float lo = 0.f, up = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * ks + key_of_reg(r, lane);
-        float p = fast_exp2(s[ks][r] * c2 - M) * invL;
-        if (diag && key > qloc) p = 0.f;
-        if (key <= qloc) lo += p; else up += p;
-      }
-    lo = wave_sum(lo);
-    up = wave_sum(up);
-    if (lane == 0) {
-      red[w][0] = lo;
-      red[w][1] = up;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float* o = lu + ((size_t)bh * nb + kb) * 2;
-      o[0] = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
-      o[1] = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
-    }
-  }
 }
 
 __global__ __launch_bounds__(NTHR) void route_finalize_kernel(
@@ -213,26 +264,41 @@ __global__ __launch_bounds__(NTHR) void route_finalize_kernel(
   }
 }
 
-template <int D>
+// Query heads per workgroup of the proxy passes: up to four (sixteen waves).
+inline int proxy_hpw(int group) { return group >= 4 ? 4 : (group >= 2 ? 2 : 1); }
+
+template <int D, int HPW>
 hipError_t route_impl(const Dims& dm, float tau, const uint16_t* q, const uint16_t* k, float* c_struct,
-                      int8_t* pattern, float* p_vert, float* p_slash, float* ws_part, float* ws_stats,
-                      float* ws_lu, hipStream_t st) {
+                      int8_t* pattern, float* p_vert, float* p_slash, const RouteBufs& wb, hipStream_t st) {
   const int ct = proxy_chunk_tiles(dm), nch = proxy_num_chunks(dm);
   const float c2 = LOG2E / sqrtf((float)D);
-  dim3 grid(nch, (unsigned)dm.bh);
-  proxy_stats_kernel<D><<<grid, NTHR, 0, st>>>(q, k, ws_part, dm.n, dm.h_q, dm.group, ct, nch, c2);
-  proxy_combine_kernel<<<(unsigned)dm.bh, BLK, 0, st>>>(ws_part, ws_stats, nch);
-  proxy_pool_kernel<D><<<grid, NTHR, 0, st>>>(q, k, ws_stats, ws_lu, dm.n, dm.h_q, dm.group, ct, c2);
-  route_finalize_kernel<<<(unsigned)dm.bh, NTHR, 0, st>>>(ws_lu, p_vert, p_slash, c_struct, pattern, dm.nb, tau);
+  dim3 grid(nch, (unsigned)(dm.batch * dm.h_kv), (unsigned)((dm.group + HPW - 1) / HPW));
+  proxy_tile_kernel<D, HPW><<<grid, NTHR * HPW, 0, st>>>(q, k, wb.part, wb.tile, dm.n, dm.h_q, dm.group, ct, nch,
+                                                         c2);
+  proxy_combine_kernel<<<(unsigned)dm.bh, BLK, 0, st>>>(wb.part, wb.stats, nch);
+  const unsigned rx = (unsigned)((dm.nb + 63) / 64);   // 16 tiles per wave
+  proxy_reduce_kernel<<<dim3(rx, (unsigned)dm.bh), NTHR, 0, st>>>(wb.tile, wb.stats, wb.lu, dm.nb);
+  route_finalize_kernel<<<(unsigned)dm.bh, NTHR, 0, st>>>(wb.lu, p_vert, p_slash, c_struct, pattern, dm.nb, tau);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t route_dispatch(const Dims& dm, float tau, const uint16_t* q, const uint16_t* k, float* c_struct,
+                          int8_t* pattern, float* p_vert, float* p_slash, const RouteBufs& wb, hipStream_t st) {
+  switch (proxy_hpw(dm.group)) {
+    case 4: return route_impl<D, 4>(dm, tau, q, k, c_struct, pattern, p_vert, p_slash, wb, st);
+    case 2: return route_impl<D, 2>(dm, tau, q, k, c_struct, pattern, p_vert, p_slash, wb, st);
+    default: return route_impl<D, 1>(dm, tau, q, k, c_struct, pattern, p_vert, p_slash, wb, st);
+  }
 }
 
 }  // namespace
 
 int proxy_chunk_tiles(const Dims& dm) {
-  // Aim at about 4096 workgroups per pass; at most 64 key tiles per workgroup.
-  const int64_t units = (int64_t)dm.nb * dm.bh;
-  int64_t ct = (units + 4095) / 4096;
+  // Aim at about 1024 workgroups (of up to four query heads) per pass; at most 64 key tiles per workgroup.
+  const int hpw = proxy_hpw(dm.group);
+  const int64_t units = (int64_t)dm.nb * dm.batch * dm.h_kv * ((dm.group + hpw - 1) / hpw);
+  int64_t ct = (units + 1023) / 1024;
   if (ct < 1) ct = 1;
   if (ct > 64) ct = 64;
   if (ct > dm.nb) ct = dm.nb;
@@ -245,11 +311,9 @@ int proxy_num_chunks(const Dims& dm) {
 }
 
 hipError_t launch_route(const Dims& dm, float tau, const uint16_t* q, const uint16_t* k, float* c_struct,
-                        int8_t* pattern, float* p_vert, float* p_slash, float* ws_part, float* ws_stats,
-                        float* ws_lu, hipStream_t st) {
-  if (dm.d == 128)
-    return route_impl<128>(dm, tau, q, k, c_struct, pattern, p_vert, p_slash, ws_part, ws_stats, ws_lu, st);
-  return route_impl<64>(dm, tau, q, k, c_struct, pattern, p_vert, p_slash, ws_part, ws_stats, ws_lu, st);
+                        int8_t* pattern, float* p_vert, float* p_slash, const RouteBufs& wb, hipStream_t st) {
+  if (dm.d == 128) return route_dispatch<128>(dm, tau, q, k, c_struct, pattern, p_vert, p_slash, wb, st);
+  return route_dispatch<64>(dm, tau, q, k, c_struct, pattern, p_vert, p_slash, wb, st);
 }
 
 }  // namespace crisp

@@ -229,14 +229,15 @@ def test_route_noalloc_validates_before_any_hip_call(lib):
     assert lib.crisp_route_noalloc(ctypes.byref(sh), ctypes.byref(cfg), P(FAKE + 4), *args[1:]) == ALIGN
     assert lib.crisp_route_noalloc(ctypes.byref(shape(n=4096 + 64)), ctypes.byref(cfg), *args) == SHAPE
     assert lib.crisp_route_noalloc(ctypes.byref(shape(batch=0)), ctypes.byref(cfg), *args) == OK
-    big = shape(batch=1, n=131072, h_q=1024, h_kv=8, d=128)
     need = ctypes.c_size_t(0)
-    assert lib.crisp_workspace_bytes(ctypes.byref(big), ctypes.byref(cfg), 0, ctypes.byref(need)) == OK
-    assert need.value > 16 << 20
-    assert lib.crisp_route_noalloc(ctypes.byref(big), ctypes.byref(cfg), *args) == SCRATCH
-    # the layers the benchmark times fit
-    for fits in (shape(n=524288, h_q=32, h_kv=8, d=128), shape(n=262144, h_q=28, h_kv=4, d=128),
-                 shape(n=1 << 20, h_q=4, h_kv=1, d=128)):
+    for big in (shape(n=524288, h_q=32, h_kv=8, d=128), shape(n=262144, h_q=28, h_kv=4, d=128),
+                shape(batch=1, n=131072, h_q=64, h_kv=8, d=128)):
+        assert lib.crisp_workspace_bytes(ctypes.byref(big), ctypes.byref(cfg), 0, ctypes.byref(need)) == OK
+        assert need.value > 64 << 20
+        assert lib.crisp_route_noalloc(ctypes.byref(big), ctypes.byref(cfg), *args) == SCRATCH
+    # up to 32 heads at 131072 tokens fit
+    for fits in (shape(n=131072, h_q=32, h_kv=8, d=128), shape(n=32768, h_q=32, h_kv=8, d=128),
+                 shape(n=4096, h_q=2, h_kv=2, d=64)):
         assert lib.crisp_workspace_bytes(ctypes.byref(fits), ctypes.byref(cfg), 0, ctypes.byref(need)) == OK
-        assert need.value <= 16 << 20, need.value
+        assert need.value <= 64 << 20, need.value
     assert lib.crisp_status_string(SCRATCH).decode().startswith("shape needs more scratch")
