@@ -85,25 +85,27 @@ def layer_attention(q_bits, k_bits, v_bits, rows_of, blocks_of, *, workers=None,
 
     ``rows_of[(b, h)]`` is that head's list of key-block rows; ``blocks_of`` maps
     (b, h) -> iterable of query blocks to compute.  Returns {(b, h, qb): array}.
+    K and V are converted once per KV head; of Q only the requested blocks' rows
+    are converted (the rest of each head's array is allocated, never touched, so
+    a long layer costs memory only for what is compared).
     """
     G = q_bits.shape[1] // k_bits.shape[1]
+    B = co.BLOCK
     jobs = [(bh, qb) for bh, qbs in blocks_of.items() for qb in qbs]
-    cache = {}
-
-    def head_arrays(bh):
+    kv, qs = {}, {}
+    for bh, qbs in blocks_of.items():
         b, h = bh
-        if bh not in cache:
-            cache[bh] = (co.bf16_to_f64(q_bits[b, h]), co.bf16_to_f64(k_bits[b, h // G]),
-                         co.bf16_to_f64(v_bits[b, h // G]))
-        return cache[bh]
-
-    # convert each head once, then fan out over its blocks
-    for bh in blocks_of:
-        head_arrays(bh)
+        if (b, h // G) not in kv:
+            kv[(b, h // G)] = (co.bf16_to_f64(k_bits[b, h // G]),
+                               co.bf16_to_f64(v_bits[b, h // G]))
+        q = np.empty(q_bits.shape[2:], dtype=np.float64)
+        for qb in qbs:
+            q[qb * B:(qb + 1) * B] = co.bf16_to_f64(q_bits[b, h, qb * B:(qb + 1) * B])
+        qs[bh] = q
 
     def one(job):
         bh, qb = job
-        q, k, v = cache[bh]
+        q, (k, v) = qs[bh], kv[(bh[0], bh[1] // G)]
         o = co.block_sparse_attention(q, k, v, rows_of[bh], q_blocks=[qb], q_rows=q_rows)[qb]
         return (bh[0], bh[1], qb), o
 
@@ -111,7 +113,8 @@ def layer_attention(q_bits, k_bits, v_bits, rows_of, blocks_of, *, workers=None,
     with _blas_limit(1):
         with ThreadPoolExecutor(min(workers, max(1, len(jobs)))) as ex:
             out = dict(ex.map(one, jobs))
-    cache.clear()
+    kv.clear()
+    qs.clear()
     return out
 
 

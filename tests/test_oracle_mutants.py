@@ -58,9 +58,11 @@ CHECKS = [getattr(pins, n) for n in dir(pins) if n.startswith("check_")]
 # Mistakes planted in copies of the layer driver, each to be caught by a driver pin.
 DRIVER_SRC = open(driver.__file__).read()
 DRIVER_MUTANTS = {
-    "attn_k_head_mod": ("co.bf16_to_f64(k_bits[b, h // G]),\n                         co.bf16_to_f64(v_bits",
-                        "co.bf16_to_f64(k_bits[b, h % k_bits.shape[1]]),\n                         co.bf16_to_f64(v_bits"),
+    "attn_k_head_mod": ("kv[(b, h // G)] = (co.bf16_to_f64(k_bits[b, h // G]),",
+                        "kv[(b, h // G)] = (co.bf16_to_f64(k_bits[b, h % k_bits.shape[1]]),"),
     "attn_v_head_mod": ("co.bf16_to_f64(v_bits[b, h // G]))", "co.bf16_to_f64(v_bits[b, h % k_bits.shape[1]]))"),
+    "attn_q_block_misread": ("q[qb * B:(qb + 1) * B] = co.bf16_to_f64(q_bits[b, h, qb * B:(qb + 1) * B])",
+                             "q[qb * B:(qb + 1) * B] = co.bf16_to_f64(q_bits[b, h, 0:B])"),
     "attn_q_rows_ignored": ("q_blocks=[qb], q_rows=q_rows)[qb]", "q_blocks=[qb])[qb]"),
     "attn_q_rows_reversed": ("q_blocks=[qb], q_rows=q_rows)[qb]",
                              "q_blocks=[qb], q_rows=None if q_rows is None else list(q_rows)[::-1])[qb]"),
