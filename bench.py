@@ -62,25 +62,49 @@ def parse():
     return ap.parse_args()
 
 
-def attn_source_sha256():
-    """Digest of the attention kernel's source: HBM counters taken on another version are not reported."""
+def source_sha256(name="attn.hip"):
+    """Digest of a kernel source file: HBM counters taken on another version are not reported."""
     import hashlib
-    path = os.path.join(ROOT, "long_context_sparse_patsearch_amd", "csrc", "attn.hip")
+    path = os.path.join(ROOT, "long_context_sparse_patsearch_amd", "csrc", name)
     with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()
+
+
+def attn_source_sha256():
+    return source_sha256("attn.hip")
+
+
+STAGE_SOURCES = {"route": "route.hip", "select": "select.hip", "attn": "attn.hip"}
+
+
+def _stored_traffic(path, workload, alpha, tiles):
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        tr = json.load(fh)
+    if tr.get("workload") == workload and tr.get("alpha") == alpha and tr.get("tiles") == tiles:
+        return tr
+    return None
 
 
 def measured_traffic(path, workload, alpha, tiles):
     """HBM bytes per attention launch from the stored counter run, or None when that run
     measured another workload, setting, tile count or attention source."""
-    if not path or not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        tr = json.load(fh)
-    if (tr.get("workload") == workload and tr.get("alpha") == alpha and tr.get("tiles") == tiles
-            and tr.get("attn_source_sha256") == attn_source_sha256()):
+    tr = _stored_traffic(path, workload, alpha, tiles)
+    if tr and tr.get("attn_source_sha256") == attn_source_sha256():
         return tr.get("bytes_per_launch")
     return None
+
+
+def measured_stage_bytes(path, workload, alpha, tiles):
+    """HBM bytes per call of each stage (route, select, the whole attention call) from the
+    stored FETCH_SIZE / WRITE_SIZE runs, for the stages whose source is unchanged since."""
+    tr = _stored_traffic(path, workload, alpha, tiles)
+    if not tr:
+        return {}
+    srcs = tr.get("sources", {})
+    return {st: b for st, b in tr.get("stages", {}).items()
+            if st in STAGE_SOURCES and srcs.get(STAGE_SOURCES[st]) == source_sha256(STAGE_SOURCES[st])}
 
 
 def _event():
@@ -140,6 +164,7 @@ class Layer:
             evs[3].record()
 
     def measure(self, alpha, steps, warmup, variant=0):
+        import numpy as np
         import torch
         cfg = self.cfg(alpha)
         for _ in range(warmup):
@@ -152,18 +177,20 @@ class Layer:
             self.step(cfg, evs[i], variant=variant)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-        st = dict(route=0.0, select=0.0, attn=0.0)
-        for e in evs:
-            st["route"] += e[0].elapsed_time(e[1]) / steps
-            st["select"] += e[1].elapsed_time(e[2]) / steps
-            st["attn"] += e[2].elapsed_time(e[3]) / steps
+        per = {"route": [e[0].elapsed_time(e[1]) for e in evs], "select": [e[1].elapsed_time(e[2]) for e in evs],
+               "attn": [e[2].elapsed_time(e[3]) for e in evs]}
+        st = {k_: sum(v_) / steps for k_, v_ in per.items()}
+        med = {k_: float(np.median(v_)) for k_, v_ in per.items()}
+        layer_med = float(np.median([sum(x) for x in zip(*per.values())]))
         tiles = int(self.s_out["row_ptr"][-1].item())
         pattern = self.r_out["pattern"].cpu().numpy()
         sh = self.wl.shape
         flop = tiles * TILE_FLOP_PER_D * sh.d
         dense_tiles = self.bh * self.nb * (self.nb + 1) // 2
         return dict(workload=self.wl.name, alpha=alpha, ms_per_layer=wall_ms,
-                    stage_ms={k_: round(v_, 4) for k_, v_ in st.items()}, tiles=tiles,
+                    stage_ms={k_: round(v_, 4) for k_, v_ in st.items()},
+                    stage_ms_median={k_: round(v_, 4) for k_, v_ in med.items()},
+                    layer_ms_median=round(layer_med, 4), tiles=tiles,
                     tile_fraction=tiles / dense_tiles, vs_heads=int(pattern.sum()),
                     pe_heads=int(len(pattern) - pattern.sum()), attn_flop=flop,
                     attn_tflops=flop / (st["attn"] * 1e-3) / 1e12, _pattern=pattern)
@@ -266,10 +293,11 @@ def mfma_rate():
 def cpu_baseline(layer, res, rp, col):
     """The fp64 oracle as it stands, on a bounded sample of the same layer.
 
-    Routing + selection run for one KV group's worth of heads (VS and PE mixed
-    as in the layer) in parallel; exact attention runs on random query blocks
-    of random heads, on the GPU's own block lists.  Both are extrapolated
-    linearly (by heads, and by selected tiles) to one whole layer."""
+    Routing + selection run for as many heads as there are workers (VS and PE
+    mixed as in the layer) in parallel; exact attention runs on four random
+    query blocks per worker, of random heads, on the GPU's own block lists.
+    Both are extrapolated linearly (by heads, and by selected tiles) to one
+    whole layer."""
     import numpy as np
 
     from oracle.driver import default_workers, layer_attention, layer_selection
@@ -283,7 +311,7 @@ def cpu_baseline(layer, res, rp, col):
     workers = default_workers()
     rng = np.random.default_rng(0)
     # heads of the sample: keep the layer's VS/PE mix
-    n_sel = min(H, workers, 8)
+    n_sel = min(H, workers)
     vs_h = [int(h) for h in np.nonzero(pattern == 1)[0]]
     pe_h = [int(h) for h in np.nonzero(pattern == 0)[0]]
     n_pe = min(len(pe_h), max(1 if pe_h else 0, round(n_sel * len(pe_h) / H)))
@@ -295,7 +323,7 @@ def cpu_baseline(layer, res, rp, col):
     # attention sample
     blocks = {}
     rows_of = {}
-    for _ in range(2 * workers):
+    for _ in range(4 * workers):
         h = int(rng.integers(0, H))
         qb = int(rng.integers(0, nb))
         blocks.setdefault((0, h), []).append(qb)
@@ -316,25 +344,29 @@ def cpu_baseline(layer, res, rp, col):
             "stage_ms": {"route_select": round(t_sel_layer * 1e3, 1), "attn": round(t_attn_layer * 1e3, 1)}}
 
 
-def stage_rates(sh, res):
-    """Algorithmic bytes / time of the routing and selection stages (GB/s).
+def stage_rates(sh, res, counted=None):
+    """Algorithmic bytes / time of the routing and selection stages (GB/s), and, where a
+    current counter run exists, the HBM bytes the counters measured / time.
 
-    route: the two proxy passes each read every KV head's K once, plus the 128
-    proxy query rows of every head.  select: PEIndex reads the Q of its PE
-    heads and the K of every KV group holding one, then passes over each PE
-    head's triangular map of N_b(N_b+1)/2 fp32 scores six times (logits
-    written; softmax read and written; three radix passes read)."""
+    route: one pass reads every KV head's K once, plus the 128 proxy query rows
+    of every head.  select: PEIndex reads the Q of its PE heads and the K of
+    every KV group holding one, then passes over each PE head's triangular map
+    of N_b(N_b+1)/2 fp32 scores six times (logits written; softmax read and
+    written; three radix passes read)."""
     kv = sh.batch * sh.h_kv * sh.n * sh.d * 2
-    route_b = 2 * kv + sh.batch * sh.h_q * 128 * sh.d * 2
+    route_b = kv + sh.batch * sh.h_q * 128 * sh.d * 2
     pe = res["pe_heads"]
-    g = sh.h_q // sh.h_kv
     pe_groups = min(sh.batch * sh.h_kv, pe)   # at most one group per PE head
     tri = sh.n_blocks * (sh.n_blocks + 1) // 2
     sel_b = pe * sh.n * sh.d * 2 + pe_groups * sh.n * sh.d * 2 + 6 * 4 * tri * pe
-    del g
-    return {"route": round(route_b / (res["stage_ms"]["route"] * 1e-3) / 1e9, 1), "route_bytes": route_b,
-            "select": round(sel_b / (res["stage_ms"]["select"] * 1e-3) / 1e9, 1), "select_bytes": sel_b,
-            "peak_hbm_gbs": 8000.0}
+    out = {"route": round(route_b / (res["stage_ms"]["route"] * 1e-3) / 1e9, 1), "route_bytes": route_b,
+           "select": round(sel_b / (res["stage_ms"]["select"] * 1e-3) / 1e9, 1), "select_bytes": sel_b,
+           "peak_hbm_gbs": 8000.0}
+    for st, b in (counted or {}).items():
+        if st in ("route", "select"):
+            out[f"{st}_counter_bytes"] = b
+            out[f"{st}_counter_gbs"] = round(b / (res["stage_ms"][st] * 1e-3) / 1e9, 1)
+    return out
 
 
 def crossover_workload(n):
@@ -510,6 +542,8 @@ def main():
                    "d": layer.wl.shape.d, "vs_heads": res["vs_heads"], "pe_heads": res["pe_heads"],
                    "parallelism": "single GPU"},
         "stage_ms": res["stage_ms"],
+        "stage_ms_median": res["stage_ms_median"],
+        "layer_ms_median": res["layer_ms_median"],
         "tiles": res["tiles"],
         "tile_fraction": round(res["tile_fraction"], 4),
         "mfma_util": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -529,7 +563,8 @@ def main():
     rows = sh.batch * sh.h_q * sh.n_blocks
     pairs = res["tiles"] * 128 * 128 - rows * (128 * 128 - 128 * 129 // 2)
     out["attn_tflops_causal_pairs"] = round(4 * sh.d * pairs / (res["stage_ms"]["attn"] * 1e-3) / 1e12, 2)
-    out["selection_gbs"] = stage_rates(sh, res)
+    out["selection_gbs"] = stage_rates(sh, res, measured_stage_bytes(args.traffic, res["workload"], alpha,
+                                                                     res["tiles"]))
     if flex:
         out["flexprefill"] = flex
     if variants:

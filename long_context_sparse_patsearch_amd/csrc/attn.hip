@@ -1102,12 +1102,12 @@ __global__ __launch_bounds__(Q64_THR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 }
 
 // V [bg][n][D] -> V^T [bg][D][n], 64-key tiles through LDS; also the largest
-// squared key norm of each KV head (kn2max[bg], as bits: non-negative floats
-// order like their bit patterns, so the integer maximum is the float maximum).
+// squared norm of the tile's 64 keys, to kn2part[bg][tile].
 template <int D>
 __global__ __launch_bounds__(NTHR) void transpose_v_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
                                                            const uint16_t* __restrict__ k,
-                                                           unsigned* __restrict__ kn2max, int n) {
+                                                           float* __restrict__ kn2part, int n) {
+  __shared__ float wmax[NTHR / 64];
   __shared__ uint16_t tile[KS][D + 2];
   const int64_t bg = blockIdx.y;
   const int key0 = blockIdx.x * KS;
@@ -1151,12 +1151,27 @@ __global__ __launch_bounds__(NTHR) void transpose_v_kernel(const uint16_t* __res
     best = fmaxf(best, acc);
   }
   best = wave_max(best);
-  if (lane_id() == 0) atomicMax(&kn2max[bg], __float_as_uint(best));
+  if (lane_id() == 0) wmax[wave_id()] = best;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    kn2part[(size_t)bg * gridDim.x + blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
-__global__ void zero_counters_kernel(int* __restrict__ c, unsigned* __restrict__ kn2max, int nkv) {
+// kn2max[bg] = the largest of the key tiles' squared norms of KV head bg.
+__global__ __launch_bounds__(NTHR) void kn2_reduce_kernel(const float* __restrict__ kn2part,
+                                                          float* __restrict__ kn2max, int tiles) {
+  __shared__ float wmax[NTHR / 64];
+  const int64_t bg = blockIdx.x;
+  float best = 0.f;
+  for (int i = threadIdx.x; i < tiles; i += NTHR) best = fmaxf(best, kn2part[(size_t)bg * tiles + i]);
+  best = wave_max(best);
+  if (lane_id() == 0) wmax[wave_id()] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) kn2max[bg] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
+__global__ void zero_counters_kernel(int* __restrict__ c) {
   if (threadIdx.x < NXCD) c[threadIdx.x] = 0;
-  for (int i = threadIdx.x; i < nkv; i += blockDim.x) kn2max[i] = 0u;
 }
 
 int cu_count() {
@@ -1174,24 +1189,29 @@ int cu_count() {
 constexpr size_t COUNTER_BYTES = 256;
 
 size_t vt_bytes(const Dims& dm) { return (size_t)dm.batch * dm.h_kv * dm.n * dm.d * 2; }
-// largest squared key norm per KV head, padded to 256 bytes
-size_t kn2_bytes(const Dims& dm) { return ((size_t)dm.batch * dm.h_kv * 4 + 255) & ~(size_t)255; }
+// largest squared key norm per KV head and per 64-key tile of each KV head, each padded to 256 bytes
+size_t kn2_bytes(const Dims& dm) {
+  const size_t bg = (size_t)dm.batch * dm.h_kv;
+  return ((bg * 4 + 255) & ~(size_t)255) + ((bg * (dm.n / KS) * 4 + 255) & ~(size_t)255);
+}
 
 template <int D, bool DENSE>
 hipError_t attn_launch(const Dims& dm, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const int64_t* row_ptr, const int32_t* col_idx, int64_t cap, void* out,
                        int out_bf16, void* ws, hipStream_t st) {
   int* counters = static_cast<int*>(ws);
-  unsigned* kn2 = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + COUNTER_BYTES);
+  const size_t bg = (size_t)dm.batch * dm.h_kv;
+  float* kn2f = reinterpret_cast<float*>(static_cast<char*>(ws) + COUNTER_BYTES);
+  float* kn2part = reinterpret_cast<float*>(static_cast<char*>(ws) + COUNTER_BYTES + ((bg * 4 + 255) & ~(size_t)255));
   uint16_t* vt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + COUNTER_BYTES + kn2_bytes(dm));
-  const float* kn2f = reinterpret_cast<const float*>(kn2);
   const float c2 = LOG2E / sqrtf((float)D);
   const Queue qd = make_queue(dm.nb, dm.bh);
   const int64_t slots = (int64_t)(cu_count() * WG_PER_CU + NXCD - 1) / NXCD * NXCD;
   const int64_t items = qd.per_queue * NXCD;
   const unsigned grid = (unsigned)(items < slots ? items : slots);
-  zero_counters_kernel<<<1, 256, 0, st>>>(counters, kn2, dm.batch * dm.h_kv);
-  transpose_v_kernel<D><<<dim3(dm.n / KS, (unsigned)(dm.batch * dm.h_kv)), NTHR, 0, st>>>(v, vt, k, kn2, dm.n);
+  zero_counters_kernel<<<1, 64, 0, st>>>(counters);
+  transpose_v_kernel<D><<<dim3(dm.n / KS, (unsigned)bg), NTHR, 0, st>>>(v, vt, k, kn2part, dm.n);
+  kn2_reduce_kernel<<<(unsigned)bg, NTHR, 0, st>>>(kn2part, kn2f, dm.n / KS);
   if constexpr (D == 128) {
     const int64_t slots64 = (int64_t)(cu_count() * Q64_WG_PER_CU + NXCD - 1) / NXCD * NXCD;
     const unsigned grid64 = (unsigned)(items < slots64 ? items : slots64);
