@@ -67,12 +67,16 @@ namespace {
 constexpr float LOG2E = 1.4426950408889634f;
 
 // The proxy pass over a chunk of key tiles, for HPW query heads of one KV
-// group at once: the workgroup is HPW slots of four waves, slot s holding the
+// group at once: the workgroup is HPW slots of two waves, slot s holding the
 // 128 proxy rows of query head split*HPW + s of the group (wave w of a slot:
-// rows 32w..32w+31), so each K tile staged in LDS serves every head of the slot
-// set and K is read once per HPW heads.  Tiles are staged through registers
-// two tiles ahead into two LDS buffers (one barrier per tile).  Slots past the
-// group's last head only help stage the tiles.
+// rows 64w..64w+63, as two 32-row MFMA tiles that share every K operand read
+// from LDS), so each K tile staged in LDS serves every head of the slot set and
+// K is read once per HPW heads.  Tiles are staged through registers two tiles
+// ahead into two LDS buffers (one barrier per tile).  Slots past the group's
+// last head only help stage the tiles.  The exponentials bound the kernel: per
+// entry it spends one maximum (half of a max3), one fused scale-and-shift, one
+// exp2 and one add, and only the diagonal 32x32 sub-tile of each row tile
+// splits its entries between the lower and upper sums.
 //
 // Per proxy row i and key tile kb it writes the tile's maximum logit m (log2
 // units) and the sums of 2^(logit - m) over the tile's lower triangle with
@@ -81,10 +85,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 // to part[bh][chunk][row].  One pass over K thus holds everything the block
 // scores need once the rows' softmax statistics are known.
 template <int D, int HPW>
-__global__ __launch_bounds__(NTHR * HPW) void proxy_tile_kernel(
+__global__ __launch_bounds__(128 * HPW) void proxy_tile_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, float* __restrict__ part,
     float* __restrict__ tilep, int n, int h_q, int group, int chunk_tiles, int nchunks, float c2) {
-  constexpr int NT = NTHR * HPW;
+  constexpr int NT = 128 * HPW;
   constexpr int CPR = Tile<D>::CPR;
   constexpr int KCH = BLK * CPR / NT;   // 16-byte K loads per thread per tile
   static_assert(KCH >= 1 && BLK * CPR % NT == 0, "tile staging");
@@ -94,17 +98,20 @@ __global__ __launch_bounds__(NTHR * HPW) void proxy_tile_kernel(
   const int h_kv = h_q / group;
   const int b = bg / h_kv, g = bg % h_kv;
   const int w = wave_id(), lane = lane_id();
-  const int slot = w >> 2, wh = w & 3;
+  const int slot = w >> 1, wh = w & 1;   // two waves per head, 64 proxy rows each (two 32-row tiles)
   const int hg = blockIdx.z * HPW + slot;
   const bool active = hg < group;
   const int64_t bh = (int64_t)b * h_q + (int64_t)g * group + (active ? hg : 0);
   const int nb = n / BLK, qb = nb - 1;
-  const int qloc = 32 * wh + (lane & 31);
+  const int qloc0 = 64 * wh + (lane & 31);   // tile t: row qloc0 + 32 t
   const uint16_t* kg = k + (size_t)bg * n * D;
 
-  bf16x8 qf[Tile<D>::NSTEP];
-  if (active) load_q_operands<D>(q + ((size_t)bh * n + (size_t)qb * BLK + 32 * wh) * D, qf);
-  float mc = -INFINITY, lc = 0.f;      // the chunk's running maximum and normaliser of the row
+  bf16x8 qf[2][Tile<D>::NSTEP];
+  if (active) {
+    load_q_operands<D>(q + ((size_t)bh * n + (size_t)qb * BLK + 64 * wh) * D, qf[0]);
+    load_q_operands<D>(q + ((size_t)bh * n + (size_t)qb * BLK + 64 * wh + 32) * D, qf[1]);
+  }
+  float mc[2] = {-INFINITY, -INFINITY}, lc[2] = {0.f, 0.f};
 
   auto load = [&](int kb, uint4 (&r)[KCH]) {
     const uint16_t* t = kg + (size_t)kb * BLK * D;
@@ -121,58 +128,94 @@ __global__ __launch_bounds__(NTHR * HPW) void proxy_tile_kernel(
       st16(lds + (c / CPR) * Tile<D>::KSTR + (c % CPR) * 8, r[i]);
     }
   };
+  // Within a 32-row tile t the rows are 32*mixblk .. 32*mixblk+31 of the proxy block, so
+  // 32-key sub-tile blk lies wholly in the lower triangle (blk < mixblk), wholly in the
+  // upper one (blk > mixblk) or on the diagonal (blk == mixblk): only that sub-tile needs
+  // the per-entry split.
   auto compute = [&](int kb, const uint16_t* lds) {
     const uint16_t* base = lds + key_row_of_lane(lane & 31) * Tile<D>::KSTR + 8 * (lane >> 5);
     const bool diag = (kb == qb);
-    float hm[2], hlo[2], hup[2];
+    float hm[2][2], hlo[2][2], hup[2][2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {   // keys 64 hf .. 64 hf + 63, relative to their own maximum
-      f32x16 s[2];
+      f32x16 s[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int ks = 2 * hf + kk;
-        f32x16 acc = {};
-        const uint16_t* pp = base + 32 * ks * Tile<D>::KSTR;
+        const uint16_t* pp = base + 32 * (2 * hf + kk) * Tile<D>::KSTR;
 #pragma unroll
-        for (int st = 0; st < Tile<D>::NSTEP; ++st) acc = mfma_32x32x16(as_bf16x8(ld16(pp + 16 * st)), qf[st], acc);
-        s[kk] = acc;
+        for (int st = 0; st < Tile<D>::NSTEP; ++st) {
+          const bf16x8 a = as_bf16x8(ld16(pp + 16 * st));   // one K read feeds both tiles
+          s[0][kk] = mfma_32x32x16(a, qf[0][st], s[0][kk]);
+          s[1][kk] = mfma_32x32x16(a, qf[1][st], s[1][kk]);
+        }
       }
-      float tmax = -INFINITY;
+      if (diag) {   // the proxy block's own tile: keys after the row are outside the causal mask
+        asm volatile("" ::: "memory");   // keep the branch: masking every tile would cost a select per entry
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kk][r] * c2;
-          if (diag && 32 * (2 * hf + kk) + key_of_reg(r, lane) > qloc) x = -INFINITY;
-          s[kk][r] = x;
-          tmax = fmaxf(tmax, x);
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * (2 * hf + kk) + key_of_reg(r, lane) > qloc0 + 32 * t) s[t][kk][r] = -INFINITY;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int mixblk = 2 * wh + t;
+        float smax = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[t][kk][r]);
+        smax = fmaxf(smax, xor_shfl(smax, 32));
+        const float tmax = smax * c2;   // c2 > 0: the maximum of the scaled logits
+        // a half the causal mask hides entirely (diagonal tile, rows < 64) sums to 0
+        const float nref = tmax == -INFINITY ? 0.f : -tmax;
+        float lo = 0.f, up = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int blk = 2 * hf + kk;
+          float bs = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(fmaf(s[t][kk][r], c2, nref));
+            s[t][kk][r] = e;
+            bs += e;
+          }
+          if (blk < mixblk) {
+            lo += bs;
+          } else if (blk > mixblk) {
+            up += bs;
+          } else {
+            asm volatile("" ::: "memory");   // as above: only this sub-tile takes the per-entry split
+            float dlo = 0.f, dup = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              if (key_of_reg(r, lane) <= (lane & 31)) dlo += s[t][kk][r]; else dup += s[t][kk][r];
+            }
+            lo += dlo;
+            up += dup;
+          }
         }
-      tmax = fmaxf(tmax, xor_shfl(tmax, 32));
-      // a half the causal mask hides entirely (diagonal tile, rows < 64) sums to 0
-      const float ref = tmax == -INFINITY ? 0.f : tmax;
-      float lo = 0.f, up = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(s[kk][r] - ref);
-          if (32 * (2 * hf + kk) + key_of_reg(r, lane) <= qloc) lo += e; else up += e;
-        }
-      hm[hf] = tmax;
-      hlo[hf] = lo + xor_shfl(lo, 32);
-      hup[hf] = up + xor_shfl(up, 32);
+        hm[t][hf] = tmax;
+        hlo[t][hf] = lo + xor_shfl(lo, 32);
+        hup[t][hf] = up + xor_shfl(up, 32);
+      }
     }
-    const float mt = fmaxf(hm[0], hm[1]);   // finite: key 0 of every tile is visible to every row
-    const float f0 = fast_exp2(hm[0] - mt), f1 = fast_exp2(hm[1] - mt);
-    const float lo = hlo[0] * f0 + hlo[1] * f1, up = hup[0] * f0 + hup[1] * f1;
-    const float mn = fmaxf(mc, mt);
-    lc = lc * fast_exp2(mc - mn) + (lo + up) * fast_exp2(mt - mn);
-    mc = mn;
-    if (lane < 32) {
-      float* o = tilep + ((size_t)bh * nb + kb) * 3 * BLK + qloc;
-      o[0] = mt;
-      o[BLK] = lo;
-      o[2 * BLK] = up;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float mt = fmaxf(hm[t][0], hm[t][1]);   // finite: key 0 of every tile is visible to every row
+      const float f0 = fast_exp2(hm[t][0] - mt), f1 = fast_exp2(hm[t][1] - mt);
+      const float lo = hlo[t][0] * f0 + hlo[t][1] * f1, up = hup[t][0] * f0 + hup[t][1] * f1;
+      const float mn = fmaxf(mc[t], mt);
+      lc[t] = lc[t] * fast_exp2(mc[t] - mn) + (lo + up) * fast_exp2(mt - mn);
+      mc[t] = mn;
+      if (lane < 32) {
+        float* o = tilep + ((size_t)bh * nb + kb) * 3 * BLK + qloc0 + 32 * t;
+        o[0] = mt;
+        o[BLK] = lo;
+        o[2 * BLK] = up;
+      }
     }
   };
 
@@ -194,9 +237,12 @@ __global__ __launch_bounds__(NTHR * HPW) void proxy_tile_kernel(
     if (active) compute(kb + 1, klds[1]);
   }
   if (active && lane < 32) {
-    float* o = part + (((size_t)bh * nchunks + chunk) * BLK + qloc) * 2;
-    o[0] = mc;
-    o[1] = lc;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float* o = part + (((size_t)bh * nchunks + chunk) * BLK + qloc0 + 32 * t) * 2;
+      o[0] = mc[t];
+      o[1] = lc[t];
+    }
   }
 }
 
@@ -273,7 +319,7 @@ hipError_t route_impl(const Dims& dm, float tau, const uint16_t* q, const uint16
   const int ct = proxy_chunk_tiles(dm), nch = proxy_num_chunks(dm);
   const float c2 = LOG2E / sqrtf((float)D);
   dim3 grid(nch, (unsigned)(dm.batch * dm.h_kv), (unsigned)((dm.group + HPW - 1) / HPW));
-  proxy_tile_kernel<D, HPW><<<grid, NTHR * HPW, 0, st>>>(q, k, wb.part, wb.tile, dm.n, dm.h_q, dm.group, ct, nch,
+  proxy_tile_kernel<D, HPW><<<grid, 128 * HPW, 0, st>>>(q, k, wb.part, wb.tile, dm.n, dm.h_q, dm.group, ct, nch,
                                                          c2);
   proxy_combine_kernel<<<(unsigned)dm.bh, BLK, 0, st>>>(wb.part, wb.stats, nch);
   const unsigned rx = (unsigned)((dm.nb + 63) / 64);   // 16 tiles per wave
