@@ -286,11 +286,26 @@ __global__ __launch_bounds__(NTHR) void pe_softmax_kernel(const int8_t* __restri
   if (pattern[bh] != 0) return;
   float* row = abar + (size_t)bh * tri + tri_off(qb);
   const int len = qb + 1;
+  // Loads four strides at a time so that each thread has four in flight; every thread still adds
+  // its entries in index order.
   float m = -INFINITY;
-  for (int j = threadIdx.x; j < len; j += NTHR) m = fmaxf(m, row[j]);
+  for (int j0 = threadIdx.x; j0 < len; j0 += 4 * NTHR) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = j0 + u * NTHR < len ? row[j0 + u * NTHR] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = fmaxf(m, v[u]);
+  }
   m = block_max(m, red);
   float s = 0.f;
-  for (int j = threadIdx.x; j < len; j += NTHR) s += fast_exp2(row[j] - m);
+  for (int j0 = threadIdx.x; j0 < len; j0 += 4 * NTHR) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = j0 + u * NTHR < len ? row[j0 + u * NTHR] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + u * NTHR < len) s += fast_exp2(v[u] - m);
+  }
   s = block_sum(s, red);
   const float fnb = (float)nb;
   for (int j = threadIdx.x; j < len; j += NTHR) row[j] = fast_exp2(row[j] - m) / s / fnb;
@@ -321,6 +336,37 @@ __device__ __forceinline__ void pass_bits(int pass, int& shift, int& width) {
   width = pass == 2 ? 10 : 11;
 }
 
+// Adds to the LDS histogram lm, by this pass's digit, the masses of the cells keys[e] for
+// e = e0, e0 + NTHR, ... < e1 (filter: only those whose bits above the digit equal prefix).  Eight
+// loads are in flight per thread.  A thread adds its cells' masses in a register while they fall in
+// the same bucket and flushes the run with one LDS atomic when the bucket changes: on a smooth map
+// most lanes of a wave hit the same bucket, and one atomic per cell would serialise on it.  The
+// sums are exact integers, so the grouping does not change them.
+__device__ __forceinline__ void hist_cells(const uint32_t* __restrict__ keys, int64_t e0, int64_t e1, bool filter,
+                                           int shift, int pshift, uint32_t dmask, uint32_t prefix, u64* lm) {
+  constexpr int U = 8;
+  uint32_t run_dig = 0;
+  u64 run_mass = 0;
+  for (int64_t e = e0; e < e1; e += U * NTHR) {
+    uint32_t kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kv[u] = e + u * NTHR < e1 ? keys[e + u * NTHR] : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t key = kv[u];
+      if (e + u * NTHR >= e1 || (filter && (key >> pshift) != prefix)) continue;
+      const uint32_t dig = (key >> shift) & dmask;
+      if (dig != run_dig) {
+        if (run_mass) atomicAdd(&lm[run_dig], run_mass);
+        run_dig = dig;
+        run_mass = 0;
+      }
+      run_mass += mass_fx(key);
+    }
+  }
+  if (run_mass) atomicAdd(&lm[run_dig], run_mass);
+}
+
 constexpr int HIST_CHUNK = 65536;
 
 __global__ __launch_bounds__(NTHR) void pe_hist_kernel(const int8_t* __restrict__ pattern, const float* __restrict__ abar,
@@ -341,12 +387,7 @@ __global__ __launch_bounds__(NTHR) void pe_hist_kernel(const int8_t* __restrict_
   const int64_t e0 = (int64_t)blockIdx.x * HIST_CHUNK;
   const int64_t e1 = e0 + HIST_CHUNK < tri ? e0 + HIST_CHUNK : tri;
   const uint32_t dmask = (1u << width) - 1u;
-  for (int64_t e = e0 + threadIdx.x; e < e1; e += NTHR) {
-    const uint32_t key = keys[e];
-    if (pass > 0 && (key >> pshift) != prefix) continue;
-    const uint32_t dig = (key >> shift) & dmask;
-    atomicAdd(&lm[dig], mass_fx(key));
-  }
+  hist_cells(keys, e0 + threadIdx.x, e1, pass > 0, shift, pshift, dmask, prefix, lm);
   __syncthreads();
   u64* gm = hmass + bh * HBINS;
   for (int i = threadIdx.x; i < HBINS; i += NTHR)
@@ -459,11 +500,7 @@ __global__ __launch_bounds__(NTHR) void pe_row_select_kernel(const int8_t* __res
     for (int i = tid; i < HBINS; i += NTHR) lm[i] = 0;
     __syncthreads();
     const uint32_t prefix = (uint32_t)sh[0];
-    for (int e = tid; e < len; e += NTHR) {
-      const uint32_t key = keys[e];
-      if (pass > 0 && (key >> pshift) != prefix) continue;
-      atomicAdd(&lm[(key >> shift) & dmask], mass_fx(key));
-    }
+    hist_cells(keys, tid, len, pass > 0, shift, pshift, dmask, prefix, lm);
     __syncthreads();
     if (tid < 64) {
       int owner = 0, found = 0;
@@ -495,6 +532,20 @@ __global__ __launch_bounds__(NTHR) void pe_row_select_kernel(const int8_t* __res
 // ------------------------------------------------------------------------------------------------
 // CSR: count per row, per-head tie allocation (PE), exclusive scan, fill.
 // ------------------------------------------------------------------------------------------------
+// Whether VS row qb keeps tile (qb, kb): tile (qb, kb) lies on block diagonal qb - kb, i.e. in
+// selected slash block nb-1-(qb-kb), or with the band in the slash block of diagonal qb-kb-1
+// (nb-(qb-kb)), whose tokens reach this tile.  Every read stays in bounds for any kb (indices are
+// clamped), so a caller can issue several without branches; kb > qb is never kept.
+__device__ __forceinline__ bool vs_cell(const uint8_t* vert, const uint8_t* slash, int nb, int qb, int kb, int band) {
+  const int kc = kb < qb ? kb : qb;
+  const int kd = kc < qb ? kc : qb - 1;
+  const uint8_t v = vert[kc], s0 = slash[nb - 1 - qb + kc], s1 = slash[nb - qb + kd];
+  return kb <= qb && (v | s0 | (band && kb < qb && s1));
+}
+
+// The CSR passes read a row 64 * CSR_U entries at a time (CSR_U loads in flight per lane).
+constexpr int CSR_U = 4;
+
 __global__ __launch_bounds__(64) void row_count_kernel(const int8_t* __restrict__ pattern, const uint8_t* __restrict__ vsflags,
                                                        const float* __restrict__ abar, const u64* __restrict__ state,
                                                        int64_t* __restrict__ rowcnt, int32_t* __restrict__ eqcnt,
@@ -508,12 +559,12 @@ __global__ __launch_bounds__(64) void row_count_kernel(const int8_t* __restrict_
     const uint8_t* vert = vsflags + (size_t)bh * 2 * nb;
     const uint8_t* slash = vert + nb;
     int cnt = 0;
-    for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
-      const int kb = kb0 + lane;
-      // tile (qb, kb) lies on block diagonal qb - kb: selected slash block nb-1-(qb-kb), or with
-      // the band, the slash block of diagonal qb-kb-1 (nb-(qb-kb)), whose tokens reach this tile
-      const bool sel = kb <= qb && (vert[kb] | slash[nb - 1 - qb + kb] | (band && kb < qb && slash[nb - qb + kb]));
-      cnt += __popcll(__ballot(sel));
+    for (int kb0 = 0; kb0 <= qb; kb0 += 64 * CSR_U) {
+      bool sel[CSR_U];
+#pragma unroll
+      for (int u = 0; u < CSR_U; ++u) sel[u] = vs_cell(vert, slash, nb, qb, kb0 + 64 * u + lane, band);
+#pragma unroll
+      for (int u = 0; u < CSR_U; ++u) cnt += __popcll(__ballot(sel[u]));
     }
     if (lane == 0) { rowcnt[r] = cnt; eqcnt[r] = 0; seltake[r] = 0; }
     return;
@@ -521,11 +572,16 @@ __global__ __launch_bounds__(64) void row_count_kernel(const int8_t* __restrict_
   const uint32_t T = rowst ? (uint32_t)rowst[2 * r] : (uint32_t)state[bh * ST_WORDS + ST_T];
   const uint32_t* keys = reinterpret_cast<const uint32_t*>(abar + (size_t)bh * tri + tri_off(qb));
   int gt = 0, eq = 0;
-  for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
-    const int kb = kb0 + lane;
-    const uint32_t key = kb <= qb ? keys[kb] : 0u;
-    gt += __popcll(__ballot(kb <= qb && key > T));
-    eq += __popcll(__ballot(kb <= qb && key == T));
+  for (int kb0 = 0; kb0 <= qb; kb0 += 64 * CSR_U) {
+    uint32_t kv[CSR_U];
+#pragma unroll
+    for (int u = 0; u < CSR_U; ++u) kv[u] = keys[min(kb0 + 64 * u + lane, qb)];
+#pragma unroll
+    for (int u = 0; u < CSR_U; ++u) {
+      const bool valid = kb0 + 64 * u + lane <= qb;
+      gt += __popcll(__ballot(valid && kv[u] > T));
+      eq += __popcll(__ballot(valid && kv[u] == T));
+    }
   }
   if (lane == 0) {
     const uint32_t dk = keys[qb];
@@ -665,12 +721,16 @@ __global__ __launch_bounds__(64) void fill_kernel(const int8_t* __restrict__ pat
   if (pattern[bh] == 1) {
     const uint8_t* vert = vsflags + (size_t)bh * 2 * nb;
     const uint8_t* slash = vert + nb;
-    for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
-      const int kb = kb0 + lane;
-      const bool sel = kb <= qb && (vert[kb] | slash[nb - 1 - qb + kb] | (band && kb < qb && slash[nb - qb + kb]));
-      const u64 bal = __ballot(sel);
-      if (sel) out[pos + __popcll(bal & below)] = kb;
-      pos += __popcll(bal);
+    for (int kb0 = 0; kb0 <= qb; kb0 += 64 * CSR_U) {
+      bool sel[CSR_U];
+#pragma unroll
+      for (int u = 0; u < CSR_U; ++u) sel[u] = vs_cell(vert, slash, nb, qb, kb0 + 64 * u + lane, band);
+#pragma unroll
+      for (int u = 0; u < CSR_U; ++u) {
+        const u64 bal = __ballot(sel[u]);
+        if (sel[u]) out[pos + __popcll(bal & below)] = kb0 + 64 * u + lane;
+        pos += __popcll(bal);
+      }
     }
     return;
   }
@@ -678,18 +738,24 @@ __global__ __launch_bounds__(64) void fill_kernel(const int8_t* __restrict__ pat
   const int take = seltake[r];
   const uint32_t* keys = reinterpret_cast<const uint32_t*>(abar + (size_t)bh * tri + tri_off(qb));
   int ties = 0;
-  for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
-    const int kb = kb0 + lane;
-    const bool valid = kb <= qb;
-    const uint32_t key = valid ? keys[kb] : 0u;
-    const bool eq = valid && key == T;
-    const u64 beq = __ballot(eq);
-    const int eqrank = ties + __popcll(beq & below);
-    const bool sel = valid && (key > T || (eq && eqrank < take) || kb == qb);
-    const u64 bal = __ballot(sel);
-    if (sel) out[pos + __popcll(bal & below)] = kb;
-    pos += __popcll(bal);
-    ties += __popcll(beq);
+  for (int kb0 = 0; kb0 <= qb; kb0 += 64 * CSR_U) {
+    uint32_t kv[CSR_U];
+#pragma unroll
+    for (int u = 0; u < CSR_U; ++u) kv[u] = keys[min(kb0 + 64 * u + lane, qb)];
+#pragma unroll
+    for (int u = 0; u < CSR_U; ++u) {
+      const int kb = kb0 + 64 * u + lane;
+      const bool valid = kb <= qb;
+      const uint32_t key = kv[u];
+      const bool eq = valid && key == T;
+      const u64 beq = __ballot(eq);
+      const int eqrank = ties + __popcll(beq & below);
+      const bool sel = valid && (key > T || (eq && eqrank < take) || kb == qb);
+      const u64 bal = __ballot(sel);
+      if (sel) out[pos + __popcll(bal & below)] = kb;
+      pos += __popcll(bal);
+      ties += __popcll(beq);
+    }
   }
 }
 
