@@ -293,11 +293,10 @@ def mfma_rate():
 def cpu_baseline(layer, res, rp, col):
     """The fp64 oracle as it stands, on a bounded sample of the same layer.
 
-    Routing + selection run for as many heads as there are workers (VS and PE
-    mixed as in the layer) in parallel; exact attention runs on four random
-    query blocks per worker, of random heads, on the GPU's own block lists.
-    Both are extrapolated linearly (by heads, and by selected tiles) to one
-    whole layer."""
+    Routing + selection run in full (every head of the layer, heads in
+    parallel over the workers); exact attention runs on sixteen random query
+    blocks per worker, of random heads, on the GPU's own block lists, and is
+    extrapolated linearly (by selected tiles) to the whole layer."""
     import numpy as np
 
     from oracle.driver import default_workers, layer_attention, layer_selection
@@ -310,20 +309,16 @@ def cpu_baseline(layer, res, rp, col):
                gamma=float(np.float32(cfg.gamma)), k_min_tokens=cfg.k_min_tokens)
     workers = default_workers()
     rng = np.random.default_rng(0)
-    # heads of the sample: keep the layer's VS/PE mix
-    n_sel = min(H, workers)
-    vs_h = [int(h) for h in np.nonzero(pattern == 1)[0]]
-    pe_h = [int(h) for h in np.nonzero(pattern == 0)[0]]
-    n_pe = min(len(pe_h), max(1 if pe_h else 0, round(n_sel * len(pe_h) / H)))
-    heads = pe_h[:n_pe] + vs_h[: n_sel - n_pe]
+    heads = list(range(H))
+    n_pe = int(np.count_nonzero(pattern == 0))
     t0 = time.perf_counter()
     layer_selection(layer.inp["q"], layer.inp["k"], heads=[(0, h) for h in heads], workers=workers, **ckw)
     t_sel = time.perf_counter() - t0
-    t_sel_layer = t_sel * H / len(heads)
+    t_sel_layer = t_sel
     # attention sample
     blocks = {}
     rows_of = {}
-    for _ in range(4 * workers):
+    for _ in range(16 * workers):
         h = int(rng.integers(0, H))
         qb = int(rng.integers(0, nb))
         blocks.setdefault((0, h), []).append(qb)
@@ -337,10 +332,10 @@ def cpu_baseline(layer, res, rp, col):
     t_attn_layer = t_attn * res["tiles"] / max(1, sampled_tiles)
     return {"value": round((t_sel_layer + t_attn_layer) * 1e3, 1), "unit": "ms/layer", "cores": workers,
             "kind": "oracle",
-            "sample": (f"routing+selection of {len(heads)} of {H} heads ({n_pe} PE) and exact attention on "
+            "sample": (f"routing+selection of all {H} heads ({n_pe} PE) in full and exact attention on "
                        f"{sum(len(v) for v in blocks.values())} random query blocks ({sampled_tiles} of "
-                       f"{res['tiles']} selected tiles) of {wl.name}, extrapolated linearly to one layer; "
-                       f"measured {t_sel:.1f}s + {t_attn:.1f}s"),
+                       f"{res['tiles']} selected tiles) of {wl.name}, the attention extrapolated linearly to "
+                       f"one layer; measured {t_sel:.1f}s + {t_attn:.1f}s"),
             "stage_ms": {"route_select": round(t_sel_layer * 1e3, 1), "attn": round(t_attn_layer * 1e3, 1)}}
 
 
