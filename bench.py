@@ -294,7 +294,7 @@ def cpu_baseline(layer, res, rp, col):
     """The fp64 oracle as it stands, on a bounded sample of the same layer.
 
     Routing + selection run in full (every head of the layer, heads in
-    parallel over the workers); exact attention runs on sixteen random query
+    parallel over the workers); exact attention runs on forty-eight random query
     blocks per worker, of random heads, on the GPU's own block lists, and is
     extrapolated linearly (by selected tiles) to the whole layer."""
     import numpy as np
@@ -318,7 +318,7 @@ def cpu_baseline(layer, res, rp, col):
     # attention sample
     blocks = {}
     rows_of = {}
-    for _ in range(16 * workers):
+    for _ in range(48 * workers):
         h = int(rng.integers(0, H))
         qb = int(rng.integers(0, nb))
         blocks.setdefault((0, h), []).append(qb)
