@@ -53,8 +53,17 @@ __global__ __launch_bounds__(NTHR) void flex_pool_k_kernel(const uint16_t* __res
   constexpr int SPLIT = NTHR / D;   // row groups per dimension
   const int dim = threadIdx.x % D, grp = threadIdx.x / D;
   const uint16_t* src = k + ((size_t)bg * n + (size_t)kb * BLK) * D + dim;
+  // rows grp, grp + SPLIT, ... in that order; sixteen loads in flight per thread
+  constexpr int PER = BLK / SPLIT, U = 16;
+  static_assert(PER % U == 0, "row batches");
   float s = 0.f;
-  for (int r = grp; r < BLK; r += SPLIT) s += bf16_to_f32(src[(size_t)r * D]);
+  for (int j0 = 0; j0 < PER; j0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = bf16_to_f32(src[(size_t)(grp + SPLIT * (j0 + u)) * D]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
+  }
   part[threadIdx.x] = s;
   __syncthreads();
   if (grp == 0) {
