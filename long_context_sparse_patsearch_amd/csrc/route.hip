@@ -310,7 +310,7 @@ __global__ __launch_bounds__(NTHR) void route_finalize_kernel(
   }
 }
 
-// Query heads per workgroup of the proxy passes: up to four (sixteen waves).
+// Query heads per workgroup of the proxy pass: up to four (eight waves).
 inline int proxy_hpw(int group) { return group >= 4 ? 4 : (group >= 2 ? 2 : 1); }
 
 template <int D, int HPW>
