@@ -2,7 +2,8 @@
 budget, the shared PEIndex and attention) against the fp64 oracle's flex_head,
 on the 4k, 32k, 128k and 512k layers (the last two are the ones the bench
 times), under the rules of parity.py: routing and selection in full, outputs
-in full at 4k and on sampled blocks (and, at 512k, sampled rows) above."""
+in full at 4k and on sampled blocks (and, at 512k, sampled rows) above; plus two
+sequences with GQA 4 at 32k, outputs in full."""
 import gc
 
 import numpy as np
@@ -53,3 +54,24 @@ def test_flex_layer_parity(idx):
     del g, q, k, v
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_flex_batch2_gqa():
+    """The FlexPrefill path with two sequences and GQA 4 (32k tokens): routing and selection in full,
+    outputs on every block of every head."""
+    from prefill_inputs import Shape, make_inputs
+    sh = Shape(2, 32768, 8, 2, 128)
+    nb = sh.n_blocks
+    inp = make_inputs(sh, vs_fraction=0.5, sink_scale=3.0, n_vert=16, seed=777)
+    q, k, v = device_inputs(inp)
+    cfg = crisp.config()
+    ckw = cfg_kwargs(cfg)
+    kw = dict(tau_jsd=TAU_JSD, gamma=ckw["gamma"], k_min_tokens=ckw["k_min_tokens"])
+    g = gpu_flex_layer(q, k, v, cfg, TAU_JSD)
+    check_csr_structure(g, sh.batch * sh.h_q, nb, crisp.max_blocks(crisp.shape_of(q, k)))
+    ora = layer_selection_flex(inp["q"], inp["k"], **kw)
+    ora, stats = check_flex_selection(g, inp, ora, kw, sh.h_q, nb)
+    _log(f"[flex batch2] selection ok: tiles={int(g['row_ptr'][-1])} exempt diffs={stats}")
+    rows = {bh: rows_of(g, bh[0] * sh.h_q + bh[1], nb) for bh in ora}
+    worst, mean = check_outputs(g["out"], inp, rows, {bh: range(nb) for bh in ora})
+    _log(f"[flex batch2] outputs ok: max-abs {worst:.2e} mean-abs {mean:.2e}")
