@@ -248,13 +248,13 @@ int flex_select(const crisp_shape* shape, const crisp_cfg* cfg, const void* q_bf
                 void* stream);
 
 /* Sequence length below which the sparse path does not pay for itself.
- * Routing and selection cost a near-fixed ~0.13 ms below 16K tokens and a
+ * Routing and selection cost a near-fixed 0.12-0.2 ms below 16K tokens and a
  * short causal map has few tiles to skip, so dense attention wins on short
  * inputs (the digest's limitations paragraph, item 7, reports the same, with
  * the crossover between 8K and 64K tokens on its GPU).  Measured on one
  * MI355X with Llama-shaped layers (32 query / 8 KV heads, d = 128, 75% VS
- * heads): dense / sparse layer time 0.93-0.98 at n = 6144 and 1.07-1.15 at
- * n = 7168 (three runs). */
+ * heads): dense / sparse layer time 0.88-0.98 at n = 6144 and 1.06-1.15 at
+ * n = 7168 (four runs). */
 #define CRISP_DENSE_BELOW_TOKENS 7168
 
 /* Which path a prefill of this shape takes: *use_dense = 1 when
