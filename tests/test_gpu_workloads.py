@@ -117,7 +117,7 @@ def test_layer_parity(idx, alpha):
 # thresholds tau = 0.15 and 0.25 of their sensitivity study.  Routing and
 # selection in full; outputs on sampled blocks (64 per head with all rows and
 # one whole VS head at 512k).
-VARIANTS = [(5, 1.5, None), (3, 1.5, None), (2, 1.0, 0.15), (2, 1.0, 0.25)]
+VARIANTS = [(5, 1.5, None), (3, 1.5, None), (4, 1.25, None), (2, 1.0, 0.15), (2, 1.0, 0.25)]
 
 
 @pytest.mark.parametrize("idx,alpha,tau", VARIANTS,
