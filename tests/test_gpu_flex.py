@@ -1,7 +1,8 @@
 """GPU parity of the FlexPrefill baseline path (JSD routing, gamma-cumsum VS
 budget, the shared PEIndex and attention) against the fp64 oracle's flex_head,
-on the 4k, 32k, 128k and 512k layers (the last two are the ones the bench
-times), under the rules of parity.py: routing and selection in full, outputs
+on the 4k, 32k, 128k, 256k (Qwen-shaped, GQA 7) and 512k layers (128k and
+512k are the ones the bench times), under the rules of parity.py: routing and
+selection in full, outputs
 in full at 4k and on sampled blocks (and, at 512k, sampled rows) above; plus two
 sequences with GQA 4 at 32k, outputs in full."""
 import gc
@@ -25,7 +26,7 @@ def _log(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 5], ids=lambda i: WORKLOADS[i].name)
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5], ids=lambda i: WORKLOADS[i].name)
 def test_flex_layer_parity(idx):
     wl = WORKLOADS[idx]
     sh = wl.shape
