@@ -1,8 +1,9 @@
 """GPU parity of the selection variants (median noise floor, slash band,
 per-row PE gamma-cumsum) against the oracle's crisp_head(floor=..., band=...,
 pe_per_row=...): routing and selection in full; outputs in full on the 4k
-layer and on sampled blocks at 32k and 128k; at 512k (where the bench times
-each variant) every variant alone, sampled rows of sampled blocks."""
+layer and on sampled blocks at 32k and 128k; all three together on the
+Qwen-shaped 256k layer (GQA 7); at 512k (where the bench times each variant)
+every variant alone; sampled rows of sampled blocks from 256k on."""
 import numpy as np
 import pytest
 
@@ -19,7 +20,8 @@ VARIANTS = {"median": (crisp.VARIANT_MEDIAN_FLOOR, "median", False, False),
             "pe_row": (crisp.VARIANT_PE_PER_ROW, "mean", False, True),
             "all": (crisp.VARIANT_MEDIAN_FLOOR | crisp.VARIANT_SLASH_BAND | crisp.VARIANT_PE_PER_ROW, "median", True,
                     True)}
-CASES = [(i, v) for i in (1, 2, 3) for v in VARIANTS] + [(5, v) for v in ("median", "band", "pe_row")]
+CASES = ([(i, v) for i in (1, 2, 3) for v in VARIANTS] + [(4, "all")]
+         + [(5, v) for v in ("median", "band", "pe_row")])
 
 
 @pytest.mark.parametrize("idx,name", CASES, ids=[f"{WORKLOADS[i].name}-{v}" for i, v in CASES])
