@@ -473,10 +473,15 @@ def main():
             a = layer.wl.alphas[0] if a is None else a
             if any(r["workload"] == layer.wl.name and r["alpha"] == a for r in results):
                 continue
-            r = layer.measure(a, args.steps, args.warmup)
+            primary = j == idx and not results
+            # the primary line times exactly --steps; the shorter layers of the 'also' list take the
+            # median of at least 10 steps (their stages are a few ms, so more steps cost little)
+            steps = args.steps if primary or layer.wl.shape.n > 131072 else max(args.steps, 10)
+            r = layer.measure(a, steps, args.warmup)
+            r["steps"] = steps
             log(f"[bench] {r['workload']} alpha={a}: {r['ms_per_layer']:.2f} ms/layer {r['stage_ms']} "
                 f"tiles={r['tiles']} attn {r['attn_tflops']:.1f} TFLOP/s")
-            r["_primary"] = (j == idx and not results)
+            r["_primary"] = primary
             results.append(r)
             if r["_primary"]:
                 rp, col = layer.host_csr()
